@@ -1,0 +1,128 @@
+/*
+ * mlp.h -- C ABI of the fused FP16 MLP inference library for MI355X (gfx950).
+ *
+ * The operation ("Profiling neural material inference", section "Experiment setup"): one complete
+ * evaluation of an affine-layer network per input row, rows independent, about a million rows per
+ * dispatch.  Layer l computes y = W_l h + b_l with FP16 weights, biases and activations and an FP32
+ * accumulator (the FP16-in / FP32-accumulate convention of "Working with Cooperative Matrices",
+ * section "Hardware Constraints and Capabilities"); the FP32 result is rounded to FP16 (nearest,
+ * ties to even) and every layer except the last is followed by the leaky ReLU
+ * max(v, v * half(0.01)) in FP16 (section "Bad versus good activation").
+ *
+ * Weights arrive in the canonical FP16 row-major form and are converted once into a device-resident
+ * layout before inference, the analogue of the page's one-time conversion to an opaque optimal
+ * layout (section "Row-major versus InferencingOptimal weights").  Matrices are tightly packed,
+ * stride = number of columns ("Working with Cooperative Matrices", section "Memory Layout").
+ *
+ * Conventions for every function:
+ *   - returns MLP_OK (0) or a negative mlp_status; never aborts, throws or exits;
+ *   - argument validation happens on the host before any HIP call, so every validation error is
+ *     reported the same way with or without a GPU;
+ *   - after an error, mlp_last_error() returns a message for the calling thread;
+ *   - "FP16" means IEEE 754 binary16 passed as its 16-bit pattern (uint16_t).
+ */
+#ifndef MLP_H
+#define MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mlp_status {
+    MLP_OK = 0,
+    MLP_ERR_INVALID_ARGUMENT = -1, /* bad shape, pointer, alignment, enum value or size          */
+    MLP_ERR_UNSUPPORTED = -2,      /* valid request that no kernel instance serves                */
+    MLP_ERR_NOT_PACKED = -3,       /* mlp_infer before a successful mlp_pack_weights              */
+    MLP_ERR_OUT_OF_MEMORY = -4,    /* device allocation failed                                   */
+    MLP_ERR_HIP = -5               /* a HIP runtime call failed; the message names it            */
+} mlp_status;
+
+/* Weight layouts ("Row-major versus InferencingOptimal weights"). */
+enum {
+    MLP_LAYOUT_ROW_MAJOR = 0, /* the canonical FP16 row-major matrices, read as they are          */
+    MLP_LAYOUT_PACKED = 1     /* converted once into MFMA-fragment order (the default)            */
+};
+
+/* Activation forms ("Bad versus good activation"); both compute the same function, bit for bit. */
+enum {
+    MLP_ACT_VECTOR = 0,    /* packed-FP16 max(v, v*half(0.01)) on whole registers (the default)  */
+    MLP_ACT_SCALARISED = 1 /* one component at a time: if (v < 0) v *= half(0.01)                */
+};
+
+#define MLP_MAX_LAYERS 8
+#define MLP_MAX_WIDTH 128
+
+/* Size in bytes of the device image mlp_pack_weights would build for this shape and layout.
+ *   n_layers  number of affine layers, 1..MLP_MAX_LAYERS
+ *   widths    n_layers + 1 entries: widths[0] = input width, widths[l] = output width of layer l,
+ *             each 1..MLP_MAX_WIDTH
+ *   layout    MLP_LAYOUT_ROW_MAJOR or MLP_LAYOUT_PACKED
+ *   out_bytes receives the size
+ * Host only; no HIP call.  MLP_ERR_UNSUPPORTED for a row-major request on a shape that only the
+ * generic (packed) kernel serves. */
+int mlp_packed_size(int n_layers, const int32_t *widths, int layout, size_t *out_bytes);
+
+/* The widths the selected kernel computes with (input width padded as the kernel reads it, every
+ * layer width padded to its tile multiple): kernel_widths receives n_layers + 1 entries.  Shapes
+ * without a dedicated kernel run on a generic kernel whose widths are all MLP_MAX_WIDTH, zero-padded.
+ * Host only; no HIP call. */
+int mlp_plan_widths(int n_layers, const int32_t *widths, int layout, int32_t *kernel_widths);
+
+/* Build the device image into a caller-owned host buffer of dst_bytes (>= mlp_packed_size).
+ *   weights   n_layers host pointers; weights[l] is [widths[l+1]][widths[l]] FP16 row-major
+ *   biases    n_layers host pointers; biases[l] is [widths[l+1]] FP16
+ * Host only; no HIP call.  Used by tests and by callers that manage device memory themselves. */
+int mlp_pack_host(int n_layers, const int32_t *widths, const uint16_t *const *weights,
+                  const uint16_t *const *biases, int layout, void *host_dst, size_t dst_bytes);
+
+/* One-time conversion: pack the weights (same arguments as mlp_pack_host) and upload them to the
+ * current HIP device.  This becomes the library's current network, replacing any previous one.
+ *   stream    hipStream_t for the upload (NULL = the default stream); the call synchronises it
+ *             before returning, so the caller may free weights and biases afterwards.
+ * Ownership: the library owns the device image until mlp_release or the next successful pack.
+ * Not thread-safe; do not re-pack while an mlp_infer on the previous network may still run.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, OUT_OF_MEMORY, HIP (previous network kept on error). */
+int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const *weights,
+                     const uint16_t *const *biases, int layout, void *stream);
+
+/* Evaluate the current network on `batch` rows: enqueue one kernel on `stream` and return.
+ *   batch    number of rows, >= 0 (0: nothing is launched, returns MLP_OK)
+ *   in_ptr   device pointer, [batch][widths[0]] FP16 row-major, 16-byte aligned
+ *   out_ptr  device pointer, [batch][widths[n_layers]] FP16 row-major, 16-byte aligned, must not
+ *            overlap in_ptr
+ *   stream   hipStream_t (NULL = the default stream)
+ * Asynchronous: the buffers must stay valid until the stream's work completes.  Must be called
+ * with the device that was current at pack time.  Uses the activation form set by
+ * mlp_set_activation_mode (default MLP_ACT_VECTOR).  Concurrent calls on different streams are
+ * safe (the weights are read-only).  A device fault, should one occur, surfaces at the caller's
+ * next synchronisation, as with any HIP kernel.
+ * Errors: INVALID_ARGUMENT, NOT_PACKED, UNSUPPORTED, HIP (launch failure). */
+int mlp_infer(int64_t batch, const void *in_ptr, void *out_ptr, void *stream);
+
+/* mlp_infer with an explicit activation form (MLP_ACT_VECTOR or MLP_ACT_SCALARISED). */
+int mlp_infer_ex(int64_t batch, const void *in_ptr, void *out_ptr, void *stream, int act_mode);
+
+/* Set the activation form mlp_infer uses (process-wide).  For A/B measurement. */
+int mlp_set_activation_mode(int act_mode);
+
+/* Name of the kernel instance that serves the current network with the given activation form,
+ * written NUL-terminated into buf (at most buf_bytes bytes, truncated if needed). */
+int mlp_kernel_name(int act_mode, char *buf, size_t buf_bytes);
+
+/* Copy the current device image back to host memory (bytes must equal its size).  For tests. */
+int mlp_debug_read_packed(void *host_dst, size_t bytes);
+
+/* Message for the last error on the calling thread ("" if none).  Valid until the next call. */
+const char *mlp_last_error(void);
+
+/* Free the current device image.  Idempotent; mlp_infer then returns MLP_ERR_NOT_PACKED. */
+void mlp_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLP_H */

@@ -1,0 +1,53 @@
+"""Build the HIP library ``libmlp.so`` in-tree with hipcc for gfx950.
+
+Usage: ``python -m mlp_neural_shading_amd.build`` (or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+CSRC = PKG / "csrc"
+LIB = PKG / "libmlp.so"
+BUILD_DIR = PKG.parent / "_build"
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    # no packed-FP32 instructions anywhere (hipcc's host pass warns that it does not know the feature)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+SOURCES = ["mlp_kernels.hip", "mlp_api.cpp", "mlp_pack.cpp"]
+
+
+def _compile(src: Path, obj: Path, extra) -> None:
+    cmd = [HIPCC, "--offload-arch=" + ARCH, *COMMON, *extra, "-x", "hip", "-c", str(src), "-o", str(obj)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src.name, " ".join(cmd), r.stderr[-8000:]))
+
+
+def build(verbose: bool = False, extra=()) -> Path:
+    BUILD_DIR.mkdir(exist_ok=True)
+    objs = [BUILD_DIR / (Path(s).stem + ".o") for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        list(ex.map(lambda so: _compile(CSRC / so[0], so[1], list(extra)), zip(SOURCES, objs)))
+    tmp = LIB.with_name(LIB.name + ".tmp%d" % os.getpid())
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr[-8000:]))
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True, extra=sys.argv[1:])

@@ -1,0 +1,345 @@
+// mlp_api.cpp -- the C ABI declared in include/mlp.h: validation, library state, HIP plumbing.
+//
+// Every argument is validated on the host before the first HIP call.  The library holds one packed
+// network (the current net) on the device that was current when it was packed.
+#include <hip/hip_runtime_api.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/mlp.h"
+#include "mlp_layout.h"
+#include "mlp_pack.h"
+#include "mlp_registry.h"
+
+using mlpk::KernelEntry;
+
+namespace {
+
+thread_local std::string t_error;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    t_error = buf;
+    return code;
+}
+
+int ok()
+{
+    t_error.clear();
+    return MLP_OK;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(MLP_ERR_HIP, "%s failed: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+struct State {
+    bool packed = false;
+    int n_layers = 0;
+    int widths[MLP_MAX_LAYERS + 1] = {};
+    int layout = MLP_LAYOUT_PACKED;
+    const KernelEntry *entry[2] = {nullptr, nullptr};  // per activation form
+    int grid_cap[2] = {0, 0};
+    void *image = nullptr;
+    size_t bytes = 0;
+    int device = -1;
+};
+
+State g_net;
+int g_act_mode = MLP_ACT_VECTOR;
+
+int check_shape(int n_layers, const int32_t *widths)
+{
+    if (n_layers < 1 || n_layers > MLP_MAX_LAYERS)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "n_layers must be in [1, %d], got %d", MLP_MAX_LAYERS, n_layers);
+    if (!widths)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "widths is NULL");
+    for (int i = 0; i <= n_layers; ++i)
+        if (widths[i] < 1 || widths[i] > MLP_MAX_WIDTH)
+            return fail(MLP_ERR_INVALID_ARGUMENT, "widths[%d] = %d is outside [1, %d]", i, (int)widths[i], MLP_MAX_WIDTH);
+    return MLP_OK;
+}
+
+int check_layout(int layout)
+{
+    if (layout != MLP_LAYOUT_ROW_MAJOR && layout != MLP_LAYOUT_PACKED)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "unknown layout %d", layout);
+    return MLP_OK;
+}
+
+int check_act(int act)
+{
+    if (act != MLP_ACT_VECTOR && act != MLP_ACT_SCALARISED)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "unknown activation mode %d", act);
+    return MLP_OK;
+}
+
+// The instance that serves (shape, layout, act): an exact-shape instance, else for the packed
+// layout with the vector activation the generic instance for that layer count, else none.
+const KernelEntry *select(int n_layers, const int32_t *widths, int layout, int act)
+{
+    int count = 0;
+    const KernelEntry *all = mlpk::registry(&count);
+    for (int i = 0; i < count; ++i) {
+        const KernelEntry &e = all[i];
+        if (e.generic || e.n_layers != n_layers || e.layout != layout || e.act != act)
+            continue;
+        bool same = true;
+        for (int k = 0; k <= n_layers; ++k)
+            same &= e.widths[k] == widths[k];
+        if (same)
+            return &e;
+    }
+    if (layout != MLP_LAYOUT_PACKED || act != MLP_ACT_VECTOR)
+        return nullptr;
+    for (int i = 0; i < count; ++i)
+        if (all[i].generic && all[i].n_layers == n_layers)
+            return &all[i];
+    return nullptr;
+}
+
+int plan(int n_layers, const int32_t *widths, int layout, const KernelEntry **out)
+{
+    int rc = check_shape(n_layers, widths);
+    if (rc == MLP_OK)
+        rc = check_layout(layout);
+    if (rc != MLP_OK)
+        return rc;
+    const KernelEntry *e = select(n_layers, widths, layout, MLP_ACT_VECTOR);
+    if (!e)
+        return fail(MLP_ERR_UNSUPPORTED, "no kernel serves this shape with the %s layout (row-major is "
+                    "compiled for the dedicated shapes only)", layout == MLP_LAYOUT_PACKED ? "packed" : "row-major");
+    *out = e;
+    return MLP_OK;
+}
+
+int check_weights(int n_layers, const uint16_t *const *weights, const uint16_t *const *biases)
+{
+    if (!weights || !biases)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "weights or biases is NULL");
+    for (int l = 0; l < n_layers; ++l)
+        if (!weights[l] || !biases[l])
+            return fail(MLP_ERR_INVALID_ARGUMENT, "weights[%d] or biases[%d] is NULL", l, l);
+    return MLP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlp_packed_size(int n_layers, const int32_t *widths, int layout, size_t *out_bytes)
+{
+    if (!out_bytes)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "out_bytes is NULL");
+    const KernelEntry *e = nullptr;
+    const int rc = plan(n_layers, widths, layout, &e);
+    if (rc != MLP_OK)
+        return rc;
+    *out_bytes = mlpk::image_bytes(n_layers, e->widths, layout);
+    return ok();
+}
+
+int mlp_plan_widths(int n_layers, const int32_t *widths, int layout, int32_t *kernel_widths)
+{
+    if (!kernel_widths)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "kernel_widths is NULL");
+    const KernelEntry *e = nullptr;
+    const int rc = plan(n_layers, widths, layout, &e);
+    if (rc != MLP_OK)
+        return rc;
+    kernel_widths[0] = mlpl::k0_pad(e->widths[0]);
+    for (int l = 1; l <= n_layers; ++l)
+        kernel_widths[l] = mlpl::round_up(e->widths[l], mlpl::kTileM);
+    return ok();
+}
+
+int mlp_pack_host(int n_layers, const int32_t *widths, const uint16_t *const *weights,
+                  const uint16_t *const *biases, int layout, void *host_dst, size_t dst_bytes)
+{
+    const KernelEntry *e = nullptr;
+    int rc = plan(n_layers, widths, layout, &e);
+    if (rc == MLP_OK)
+        rc = check_weights(n_layers, weights, biases);
+    if (rc != MLP_OK)
+        return rc;
+    const size_t need = mlpk::image_bytes(n_layers, e->widths, layout);
+    if (!host_dst)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "host_dst is NULL");
+    if (dst_bytes < need)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "host_dst holds %zu bytes, the image needs %zu", dst_bytes, need);
+    mlpk::pack_image(n_layers, widths, e->widths, weights, biases, layout, (uint8_t *)host_dst);
+    return ok();
+}
+
+int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const *weights,
+                     const uint16_t *const *biases, int layout, void *stream)
+{
+    const KernelEntry *e = nullptr;
+    int rc = plan(n_layers, widths, layout, &e);
+    if (rc == MLP_OK)
+        rc = check_weights(n_layers, weights, biases);
+    if (rc != MLP_OK)
+        return rc;
+
+    State next;
+    next.n_layers = n_layers;
+    for (int i = 0; i <= n_layers; ++i)
+        next.widths[i] = widths[i];
+    next.layout = layout;
+    next.entry[MLP_ACT_VECTOR] = e;
+    next.entry[MLP_ACT_SCALARISED] = select(n_layers, widths, layout, MLP_ACT_SCALARISED);
+    next.bytes = mlpk::image_bytes(n_layers, e->widths, layout);
+    std::vector<uint8_t> host(next.bytes);
+    mlpk::pack_image(n_layers, widths, e->widths, weights, biases, layout, host.data());
+
+    hipError_t err = hipGetDevice(&next.device);
+    if (err != hipSuccess)
+        return hip_fail(err, "hipGetDevice");
+    int cus = 0;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, next.device);
+    if (err != hipSuccess)
+        return hip_fail(err, "hipDeviceGetAttribute(multiProcessorCount)");
+    for (int a = 0; a < 2; ++a) {
+        const KernelEntry *k = next.entry[a];
+        if (!k)
+            continue;
+        int blocks = 0;
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k->func, k->threads, 0);
+        if (err != hipSuccess)
+            return hip_fail(err, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+        if (blocks < 1)
+            return fail(MLP_ERR_UNSUPPORTED, "kernel %s cannot be resident on this device", k->name);
+        next.grid_cap[a] = blocks * cus;
+    }
+    err = hipMalloc(&next.image, next.bytes);
+    if (err != hipSuccess) {
+        const int code = err == hipErrorOutOfMemory ? MLP_ERR_OUT_OF_MEMORY : MLP_ERR_HIP;
+        return fail(code, "hipMalloc(%zu) failed: %s", next.bytes, hipGetErrorString(err));
+    }
+    err = hipMemcpyAsync(next.image, host.data(), next.bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (err == hipSuccess)
+        err = hipStreamSynchronize((hipStream_t)stream);
+    if (err != hipSuccess) {
+        (void)hipFree(next.image);
+        return hip_fail(err, "uploading the weight image");
+    }
+    next.packed = true;
+    if (g_net.packed)
+        (void)hipFree(g_net.image);
+    g_net = next;
+    return ok();
+}
+
+int mlp_infer_ex(int64_t batch, const void *in_ptr, void *out_ptr, void *stream, int act_mode)
+{
+    if (batch < 0)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "batch must be >= 0, got %lld", (long long)batch);
+    int rc = check_act(act_mode);
+    if (rc != MLP_OK)
+        return rc;
+    if (!g_net.packed)
+        return fail(MLP_ERR_NOT_PACKED, "no network: call mlp_pack_weights first");
+    const KernelEntry *e = g_net.entry[act_mode];
+    if (!e)
+        return fail(MLP_ERR_UNSUPPORTED, "the %s activation form is compiled for the dedicated shapes only",
+                    act_mode == MLP_ACT_SCALARISED ? "scalarised" : "vector");
+    if (batch == 0)
+        return ok();
+    const int w0 = g_net.widths[0], wL = g_net.widths[g_net.n_layers];
+    if (batch > INT64_MAX / (2 * MLP_MAX_WIDTH))
+        return fail(MLP_ERR_INVALID_ARGUMENT, "batch %lld is too large", (long long)batch);
+    if (!in_ptr || !out_ptr)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "in_ptr or out_ptr is NULL");
+    if (((uintptr_t)in_ptr | (uintptr_t)out_ptr) & 15)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "in_ptr and out_ptr must be 16-byte aligned");
+    const uintptr_t i0 = (uintptr_t)in_ptr, i1 = i0 + (uintptr_t)(batch * w0 * 2);
+    const uintptr_t o0 = (uintptr_t)out_ptr, o1 = o0 + (uintptr_t)(batch * wL * 2);
+    if (i0 < o1 && o0 < i1)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "in and out buffers overlap");
+
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return hip_fail(err, "hipGetDevice");
+    if (dev != g_net.device)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "current device %d is not the device %d the network was packed on",
+                    dev, g_net.device);
+
+    const int64_t rows_per_block = (int64_t)e->rows_per_wave * (e->threads / 64);
+    const int64_t blocks = (batch + rows_per_block - 1) / rows_per_block;
+    const int grid = (int)(blocks < g_net.grid_cap[act_mode] ? blocks : g_net.grid_cap[act_mode]);
+    mlpk::LaunchArgs a;
+    a.x = (const uint16_t *)in_ptr;
+    a.y = (uint16_t *)out_ptr;
+    a.image = (const uint8_t *)g_net.image;
+    a.batch = batch;
+    a.w0 = w0;
+    a.wL = wL;
+    err = e->launch(a, grid, (hipStream_t)stream);
+    if (err != hipSuccess)
+        return hip_fail(err, "kernel launch");
+    return ok();
+}
+
+int mlp_infer(int64_t batch, const void *in_ptr, void *out_ptr, void *stream)
+{
+    return mlp_infer_ex(batch, in_ptr, out_ptr, stream, g_act_mode);
+}
+
+int mlp_set_activation_mode(int act_mode)
+{
+    const int rc = check_act(act_mode);
+    if (rc != MLP_OK)
+        return rc;
+    g_act_mode = act_mode;
+    return ok();
+}
+
+int mlp_kernel_name(int act_mode, char *buf, size_t buf_bytes)
+{
+    int rc = check_act(act_mode);
+    if (rc != MLP_OK)
+        return rc;
+    if (!buf || buf_bytes == 0)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "buf is NULL or empty");
+    if (!g_net.packed)
+        return fail(MLP_ERR_NOT_PACKED, "no network: call mlp_pack_weights first");
+    const KernelEntry *e = g_net.entry[act_mode];
+    if (!e)
+        return fail(MLP_ERR_UNSUPPORTED, "no kernel for this activation form on the current network");
+    snprintf(buf, buf_bytes, "%s", e->name);
+    return ok();
+}
+
+int mlp_debug_read_packed(void *host_dst, size_t bytes)
+{
+    if (!g_net.packed)
+        return fail(MLP_ERR_NOT_PACKED, "no network: call mlp_pack_weights first");
+    if (!host_dst || bytes != g_net.bytes)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "need a host buffer of exactly %zu bytes", g_net.bytes);
+    const hipError_t err = hipMemcpy(host_dst, g_net.image, bytes, hipMemcpyDeviceToHost);
+    if (err != hipSuccess)
+        return hip_fail(err, "hipMemcpy(device image -> host)");
+    return ok();
+}
+
+const char *mlp_last_error(void) { return t_error.c_str(); }
+
+void mlp_release(void)
+{
+    if (g_net.packed)
+        (void)hipFree(g_net.image);
+    g_net = State();
+}
+
+}  // extern "C"

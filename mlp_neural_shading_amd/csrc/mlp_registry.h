@@ -1,0 +1,40 @@
+// mlp_registry.h -- the table of compiled kernel instances and how the host launches them.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mlpk {
+
+enum Layout { kRowMajor = 0, kPacked = 1 };
+enum Act { kVector = 0, kScalarised = 1 };
+
+// Everything one launch needs; passed by value as the kernel argument.
+struct LaunchArgs {
+    const uint16_t *x;     // [batch][w0] FP16
+    uint16_t *y;           // [batch][wL] FP16
+    const uint8_t *image;  // device weight image
+    int64_t batch;
+    int32_t w0;            // caller's input width (row stride of x)
+    int32_t wL;            // caller's output width (row stride of y)
+};
+
+struct KernelEntry {
+    const char *name;
+    int n_layers;
+    int widths[9];      // exact instance: the widths it serves; generic: all 128 (any shape <= 128)
+    bool generic;
+    int layout;
+    int act;
+    int threads;        // threads per workgroup
+    int rows_per_wave;  // rows one wave evaluates per loop iteration
+    bool weights_in_lds;
+    hipError_t (*launch)(const LaunchArgs &, int grid, hipStream_t);
+    const void *func;   // kernel symbol, for occupancy queries
+};
+
+// All compiled instances.
+const KernelEntry *registry(int *count);
+
+}  // namespace mlpk

@@ -1,0 +1,163 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports every function that
+include/mlp.h declares, validation errors come back before any HIP call, and the packer's images
+follow the documented layout (checked by an unpacker written here from the layout description, not
+from the library's code)."""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+from mlp_neural_shading_amd import binding as B
+from mlp_neural_shading_amd import workloads
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "mlp.h"
+
+
+def _have_gpu() -> bool:
+    try:
+        import torch
+
+        return torch.cuda.device_count() > 0
+    except Exception:  # pragma: no cover
+        return False
+
+
+def test_library_exports_every_declared_function():
+    decls = set(re.findall(r"^\s*(?:int|void|const char \*)\s*(mlp_\w+)\s*\(", HEADER.read_text(), re.M))
+    assert decls == set(B.EXPORTED)
+    L = B.lib()
+    for name in decls:
+        assert hasattr(L, name), name
+
+
+def _err(fn, *args):
+    with pytest.raises(B.MlpError) as e:
+        fn(*args)
+    return e.value.code
+
+
+def test_shape_validation():
+    assert _err(B.mlp_packed_size, [], 1) == B.MLP_ERR_INVALID_ARGUMENT            # n_layers 0 (one width)
+    assert _err(B.mlp_packed_size, [4] * 10, 1) == B.MLP_ERR_INVALID_ARGUMENT      # 9 layers
+    assert _err(B.mlp_packed_size, [4, 0, 4], 1) == B.MLP_ERR_INVALID_ARGUMENT
+    assert _err(B.mlp_packed_size, [4, 129, 4], 1) == B.MLP_ERR_INVALID_ARGUMENT
+    assert _err(B.mlp_packed_size, [4, 4], 7) == B.MLP_ERR_INVALID_ARGUMENT        # unknown layout
+    assert "widths[1]" in B.mlp_last_error() or "layout" in B.mlp_last_error()
+    # row-major is compiled only for the dedicated shapes
+    assert _err(B.mlp_packed_size, [5, 7, 3], B.MLP_LAYOUT_ROW_MAJOR) == B.MLP_ERR_UNSUPPORTED
+    assert B.mlp_packed_size([5, 7, 3], B.MLP_LAYOUT_PACKED) > 0
+
+
+def test_null_arguments_are_rejected():
+    L = B.lib()
+    w = np.array([4, 4], np.int32)
+    assert L.mlp_packed_size(1, w.ctypes.data, 1, None) == B.MLP_ERR_INVALID_ARGUMENT
+    assert L.mlp_packed_size(1, None, 1, ctypes.byref(ctypes.c_size_t())) == B.MLP_ERR_INVALID_ARGUMENT
+    assert L.mlp_pack_host(1, w.ctypes.data, None, None, 1, None, 0) == B.MLP_ERR_INVALID_ARGUMENT
+    assert L.mlp_plan_widths(1, w.ctypes.data, 1, None) == B.MLP_ERR_INVALID_ARGUMENT
+    assert L.mlp_kernel_name(0, None, 0) == B.MLP_ERR_INVALID_ARGUMENT
+    assert L.mlp_set_activation_mode(2) == B.MLP_ERR_INVALID_ARGUMENT
+    # a too-small destination buffer
+    Ws, bs = workloads.init_weights([4, 4])
+    ws = B._Weights(Ws, bs)
+    dst = np.zeros(16, np.uint8)
+    assert L.mlp_pack_host(1, w.ctypes.data, ws.wp, ws.bp, 1, dst.ctypes.data, 16) == B.MLP_ERR_INVALID_ARGUMENT
+
+
+def test_infer_before_pack_and_bad_batch():
+    B.mlp_release()
+    B.mlp_release()  # idempotent
+    assert _err(B.mlp_infer, 16, 0x1000, 0x2000) == B.MLP_ERR_NOT_PACKED
+    assert _err(B.mlp_infer, -1, 0x1000, 0x2000) == B.MLP_ERR_INVALID_ARGUMENT
+    assert _err(B.mlp_infer_ex, 16, 0x1000, 0x2000, None, 9) == B.MLP_ERR_INVALID_ARGUMENT
+    assert _err(B.mlp_kernel_name, 0) == B.MLP_ERR_NOT_PACKED
+    assert _err(B.mlp_debug_read_packed, 16) == B.MLP_ERR_NOT_PACKED
+
+
+@pytest.mark.skipif(_have_gpu(), reason="checks the error path taken when no GPU is visible")
+def test_pack_without_a_device_reports_hip_error():
+    Ws, bs = workloads.init_weights([4, 4])
+    with pytest.raises(B.MlpError) as e:
+        B.mlp_pack_weights(Ws, bs)
+    assert e.value.code == B.MLP_ERR_HIP
+    assert "hip" in str(e.value).lower()
+
+
+def test_plan_widths():
+    assert B.mlp_plan_widths(workloads.get("small").widths) == [32, 32, 32, 32, 32, 32, 32, 32, 16]
+    assert B.mlp_plan_widths(workloads.get("page").widths) == [32] + [64] * 7 + [16]
+    assert B.mlp_plan_widths([2, 2, 1]) == [128, 128, 128]  # generic kernel, zero-padded
+
+
+# ---- an independent reading of the packed layout ---------------------------------------------
+#
+# Packed image, per layer: A fragments [mt][kb][lane][8] FP16 then bias tiles [mt][g][4] FP32, where
+# lane = 16 g + m holds row 16 mt + m; slot j of block kb holds input feature
+#   layer 0:  32 kb + 8 g + j
+#   layer >0: 16 (2 kb + j // 4) + 4 g + j % 4
+# and the bias tile entry (mt, g, i) is b[16 mt + 4 g + i].  Anything outside the real matrix is 0.
+
+def _unpack(image, kw, widths):
+    L = len(widths) - 1
+    off = 0
+    Ws, bs = [], []
+    for l in range(L):
+        MT = -(-kw[l + 1] // 16)
+        KB = (-(-kw[0] // 32) * 32) // 32 if l == 0 else -(-(-(-kw[l] // 16)) // 2)
+        A = image[off:off + MT * KB * 1024].view(np.uint16).reshape(MT, KB, 4, 16, 8)
+        off += MT * KB * 1024
+        bias = image[off:off + MT * 64].view(np.float32).reshape(MT, 4, 4)
+        off += MT * 64
+        full = np.zeros((MT * 16, KB * 32), np.uint16)
+        for mt in range(MT):
+            for kb in range(KB):
+                for g in range(4):
+                    for j in range(8):
+                        f = 32 * kb + 8 * g + j if l == 0 else 16 * (2 * kb + j // 4) + 4 * g + j % 4
+                        full[16 * mt:16 * mt + 16, f] = A[mt, kb, g, :, j]
+        Ws.append(full)
+        bs.append(bias.reshape(-1))
+    assert off == image.size
+    return Ws, bs
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS) + ["generic-5-7-3"])
+def test_packed_image_layout(name):
+    if name.startswith("generic"):
+        widths = (5, 7, 3)
+        Ws, bs = workloads.init_weights(widths, seed=3)
+    else:
+        widths = workloads.WORKLOADS[name].widths
+        Ws, bs = workloads.init_weights(widths)
+    kw = B.mlp_plan_widths(widths)
+    image = B.mlp_pack_host(Ws, bs, B.MLP_LAYOUT_PACKED)
+    assert image.size == B.mlp_packed_size(widths)
+    UW, Ub = _unpack(image, kw, widths)
+    for l in range(len(widths) - 1):
+        wout, win = Ws[l].shape
+        got = UW[l]
+        assert np.array_equal(got[:wout, :win], Ws[l].view(np.uint16)), l
+        pad = got.copy()
+        pad[:wout, :win] = 0
+        assert not pad.any(), "padding must be zero"
+        assert np.array_equal(Ub[l][:wout], bs[l].astype(np.float32)), l  # exact widening
+        assert not Ub[l][wout:].any()
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_row_major_image_is_verbatim(name):
+    widths = workloads.WORKLOADS[name].widths
+    Ws, bs = workloads.init_weights(widths)
+    image = B.mlp_pack_host(Ws, bs, B.MLP_LAYOUT_ROW_MAJOR)
+    off = 0
+    for W, b in zip(Ws, bs):
+        n = W.size * 2
+        assert np.array_equal(image[off:off + n].view(np.uint16), W.view(np.uint16).ravel())
+        off += -(-n // 16) * 16
+        n = b.size * 2
+        assert np.array_equal(image[off:off + n].view(np.uint16), b.view(np.uint16))
+        off += -(-n // 16) * 16
+    assert off == image.size

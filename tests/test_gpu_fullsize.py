@@ -1,0 +1,155 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark times, on rows
+the oracle can compute one by one; plus properties that hold at any size (all outputs finite,
+replicated inputs give identical outputs, results do not depend on the batch)."""
+import numpy as np
+import pytest
+
+from conftest import host_threads
+from gpu_util import compare, log
+from mlp_neural_shading_amd import binding as B
+from mlp_neural_shading_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_full(wl, act=B.MLP_ACT_VECTOR, layout=B.MLP_LAYOUT_PACKED):
+    import torch
+
+    Ws, bs = wl.weights()
+    x = wl.inputs(device="cuda")
+    y = torch.empty((wl.batch, wl.widths[-1]), dtype=torch.float16, device="cuda")
+    B.mlp_pack_weights(Ws, bs, layout)
+    B.mlp_infer_ex(wl.batch, x.data_ptr(), y.data_ptr(), torch.cuda.current_stream().cuda_stream, act)
+    torch.cuda.synchronize()
+    return Ws, bs, x, y
+
+
+def _rows_bits(t, idx):
+    import torch
+
+    sel = t.index_select(0, torch.as_tensor(idx, device=t.device))
+    return sel.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _sample(wl, n_random, edge, extra=()):
+    rng = np.random.default_rng(77)
+    idx = np.concatenate([np.arange(edge), np.arange(wl.batch - edge, wl.batch),
+                          rng.integers(0, wl.batch, size=n_random), np.asarray(extra, dtype=np.int64)])
+    return np.unique(idx[(idx >= 0) & (idx < wl.batch)])
+
+
+def test_page_workload_full(oracle_mod):
+    """1,048,576 evals = 65,536 inputs x 16: every unique row against the oracle, every replica
+    bit-identical to the first (each evaluation is independent and deterministic)."""
+    import torch
+
+    wl = workloads.get("page")
+    log("full", wl.name)
+    Ws, bs, x, y = _run_full(wl)
+    assert bool(torch.isfinite(y).all())
+    u = wl.unique_rows
+    first = y[:u]
+    for r in range(1, wl.replicas):
+        assert torch.equal(y[r * u:(r + 1) * u], first), "replica %d differs" % r
+    xb = x[:u].cpu().view(torch.int16).numpy().view(np.uint16)
+    ref = oracle_mod.mlp_forward(Ws, bs, xb, threads=host_threads())
+    stats = compare(first.cpu().view(torch.int16).numpy().view(np.uint16), ref, what=wl.name)
+    log("   ", stats)
+    # the other three variants on the full dispatch give the same bits
+    for layout, act in [(B.MLP_LAYOUT_PACKED, B.MLP_ACT_SCALARISED), (B.MLP_LAYOUT_ROW_MAJOR, B.MLP_ACT_VECTOR)]:
+        _, _, _, y2 = _run_full(wl, act=act, layout=layout)
+        assert torch.equal(y2, y), (layout, act)
+
+
+@pytest.mark.parametrize("name,n_random,edge", [("small", 0, 4096), ("hetero", 24576, 1024), ("wide", 6144, 512)])
+def test_full_size_sampled(oracle_mod, name, n_random, edge):
+    import torch
+
+    wl = workloads.get(name)
+    log("full", wl.name)
+    Ws, bs, x, y = _run_full(wl)
+    assert bool(torch.isfinite(y).all())
+    idx = _sample(wl, n_random, edge)
+    ref = oracle_mod.mlp_forward_rows(Ws, bs, _rows_bits(x, idx), np.arange(idx.size), threads=host_threads())
+    log("   ", compare(_rows_bits(y, idx), ref, what=wl.name), "rows checked", idx.size)
+
+
+def test_streaming_workload_full(oracle_mod):
+    """67,108,864 distinct inputs (8 GiB in, 2 GiB out): sampled rows including those whose input
+    bytes straddle each 2 GiB boundary (64-bit addressing)."""
+    import torch
+
+    wl = workloads.get("stream")
+    log("full", wl.name, "(8 GiB of input)")
+    Ws, bs, x, y = _run_full(wl)
+    assert bool(torch.isfinite(y).all())
+    row_bytes = 2 * wl.widths[0]
+    edges = []
+    for k in (1, 2, 3):
+        r = (k << 31) // row_bytes
+        edges += list(range(r - 64, r + 64))
+    idx = _sample(wl, 16384, 512, extra=edges)
+    ref = oracle_mod.mlp_forward_rows(Ws, bs, _rows_bits(x, idx), np.arange(idx.size), threads=host_threads())
+    log("   ", compare(_rows_bits(y, idx), ref, what=wl.name), "rows checked", idx.size)
+    del x, y
+    torch.cuda.empty_cache()
+
+
+def test_batch_independence_and_determinism():
+    """Row r's output depends only on input row r: any batch prefix and any repeat give the same
+    bits (the grid size changes with the batch)."""
+    import torch
+
+    wl = workloads.get("hetero")
+    Ws, bs = wl.weights()
+    x = wl.inputs(device="cuda", rows=200003)
+    B.mlp_pack_weights(Ws, bs)
+    s = torch.cuda.current_stream().cuda_stream
+    full = torch.empty((x.shape[0], wl.widths[-1]), dtype=torch.float16, device="cuda")
+    B.mlp_infer(x.shape[0], x.data_ptr(), full.data_ptr(), s)
+    again = torch.empty_like(full)
+    B.mlp_infer(x.shape[0], x.data_ptr(), again.data_ptr(), s)
+    torch.cuda.synchronize()
+    assert torch.equal(full, again)
+    for n in (1, 64, 1000, 65537, 131072):
+        part = torch.full((n, wl.widths[-1]), float("nan"), dtype=torch.float16, device="cuda")
+        B.mlp_infer(n, x.data_ptr(), part.data_ptr(), s)
+        torch.cuda.synchronize()
+        assert torch.equal(part, full[:n]), n
+    # an offset start (rows 1000..) is the same computation on the same rows
+    off = 1024
+    part = torch.empty((5000, wl.widths[-1]), dtype=torch.float16, device="cuda")
+    B.mlp_infer(5000, x[off:].data_ptr(), part.data_ptr(), s)
+    torch.cuda.synchronize()
+    assert torch.equal(part, full[off:off + 5000])
+
+
+def test_boundary_errors_on_device():
+    import torch
+
+    wl = workloads.get("small")
+    Ws, bs = wl.weights()
+    B.mlp_pack_weights(Ws, bs)
+    x = wl.inputs(device="cuda", rows=64)
+    y = torch.empty((64, 4), dtype=torch.float16, device="cuda")
+    B.mlp_infer(0, x.data_ptr(), y.data_ptr())  # batch 0: nothing launched
+    with pytest.raises(B.MlpError) as e:
+        B.mlp_infer(63, x.data_ptr() + 2, y.data_ptr())
+    assert e.value.code == B.MLP_ERR_INVALID_ARGUMENT and "aligned" in str(e.value)
+    with pytest.raises(B.MlpError) as e:
+        B.mlp_infer(64, x.data_ptr(), x.data_ptr() + 16)
+    assert e.value.code == B.MLP_ERR_INVALID_ARGUMENT and "overlap" in str(e.value)
+    # the device image round-trips to the host image
+    n = B.mlp_packed_size(wl.widths)
+    assert np.array_equal(B.mlp_debug_read_packed(n), B.mlp_pack_host(Ws, bs))
+    assert "16-32x7-4" in B.mlp_kernel_name(B.MLP_ACT_VECTOR)
+    # a generic-shape net has no scalarised kernel
+    Wg, bg = workloads.init_weights((5, 7, 3))
+    B.mlp_pack_weights(Wg, bg)
+    with pytest.raises(B.MlpError) as e:
+        B.mlp_infer_ex(4, x.data_ptr(), y.data_ptr(), None, B.MLP_ACT_SCALARISED)
+    assert e.value.code == B.MLP_ERR_UNSUPPORTED
+    B.mlp_release()
+    with pytest.raises(B.MlpError) as e:
+        B.mlp_infer(4, x.data_ptr(), y.data_ptr())
+    assert e.value.code == B.MLP_ERR_NOT_PACKED
