@@ -132,11 +132,16 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
+    # The timed region: exactly --steps back-to-back steps, synchronised on both sides.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    launch_ms = time_dispatches(torch, step, args.steps)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # The same steps again, each bracketed by HIP events on the launch stream: kernel durations.
+    launch_ms = time_dispatches(torch, step, args.steps)
     mean_launch_ms = statistics.fmean(launch_ms)
     achieved_tflops = flops_per_launch / (mean_launch_ms * 1e-3) / 1e12
 

@@ -26,8 +26,12 @@ COMMON = [
 SOURCES = ["mlp_kernels.hip", "mlp_api.cpp", "mlp_pack.cpp"]
 
 
+INCLUDE = PKG.parent / "include"
+
+
 def _compile(src: Path, obj: Path, extra) -> None:
-    cmd = [HIPCC, "--offload-arch=" + ARCH, *COMMON, *extra, "-x", "hip", "-c", str(src), "-o", str(obj)]
+    cmd = [HIPCC, "--offload-arch=" + ARCH, *COMMON, "-I", str(INCLUDE), *extra, "-x", "hip", "-c", str(src),
+           "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src.name, " ".join(cmd), r.stderr[-8000:]))

@@ -10,7 +10,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/mlp.h"
+#include "mlp.h"
 #include "mlp_layout.h"
 #include "mlp_pack.h"
 #include "mlp_registry.h"

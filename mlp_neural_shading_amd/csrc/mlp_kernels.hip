@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "mlp_layout.h"
 #include "mlp_registry.h"
@@ -192,7 +193,6 @@ struct Body {
             }
             layer<l + 1>(wb, Bout, a, row0, lane);
         } else {
-            const int g = lane >> 4, n = lane & 15;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 h8 af[KB];
@@ -209,57 +209,91 @@ struct Body {
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
                         acc[t] = mfma(af[kb], Bin[kb][t], acc[t]);
-                const int c = 16 * mt + 4 * g;  // first output feature this lane holds
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const h4 v = __builtin_convertvector(acc[t], h4);
-                    const int64_t row = row0 + 16 * t + n;
-                    if (row < a.batch) {
-                        if constexpr (kVecOut) {
-                            constexpr int wl = N::w[L];
-                            if (c < wl)
-                                *(h4 *)((_Float16 *)a.y + row * wl + c) = v;
-                        } else {
-                            _Float16 *yr = (_Float16 *)a.y + row * a.wL;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                if (c + i < a.wL)
-                                    yr[c + i] = v[i];
-                        }
-                    }
-                }
+                store_outputs(acc, mt, a, row0, lane, std::make_integer_sequence<int, NT>());
             }
         }
     }
 
     // ---- input rows -> layer-0 B fragments --------------------------------------------------
+    //
+    // Written as one straight-line body per sample tile (an index-sequence expansion, not a loop):
+    // a loop over tiles with the "row < batch" test gets peeled by the compiler into a run-time loop
+    // with dynamically indexed fragment registers.  Loads are branch-free: the address is clamped to
+    // a valid row and the value replaced by zero for rows past the batch.
 
-    static __device__ __forceinline__ void load_inputs(h8 (&B)[N::KB(0)][NT], const LaunchArgs &a,
-                                                       int64_t row0, int lane)
+    template <int t>
+    static __device__ __forceinline__ void load_tile(h8 (&B)[N::KB(0)][NT], const LaunchArgs &a, int64_t row0,
+                                                     int lane)
     {
         const int g = lane >> 4, n = lane & 15;
+        const int64_t row = row0 + 16 * t + n;
+        const bool live = row < a.batch;
+        const int64_t rr = live ? row : a.batch - 1;
+        constexpr int KB0 = N::KB(0);  // a constant expression, so the loop below fully unrolls
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int64_t row = row0 + 16 * t + n;
-            const bool live = row < a.batch;
-#pragma unroll
-            for (int kb = 0; kb < N::KB(0); ++kb) {
-                const int c = 32 * kb + 8 * g;
-                h8 v = (h8)(_Float16)0;  // padded slots are zero in registers, never loaded
-                if constexpr (kVecIn) {
-                    constexpr int w0 = N::w[0];
-                    if (live && c < w0)
-                        v = *(const h8 *)((const _Float16 *)a.x + row * w0 + c);
+        for (int kb = 0; kb < KB0; ++kb) {
+            const int c = 32 * kb + 8 * g;
+            h8 v = (h8)(_Float16)0;  // padded slots are zero in registers, never loaded
+            if constexpr (kVecIn) {
+                constexpr int w0 = N::w[0];
+                if (32 * kb + 32 <= w0) {  // whole block inside the row (folds after unrolling)
+                    v = *(const h8 *)((const _Float16 *)a.x + rr * w0 + c);
+                    v = live ? v : (h8)(_Float16)0;
                 } else {
-                    const _Float16 *xr = (const _Float16 *)a.x + row * a.w0;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        if (live && c + j < a.w0)
-                            v[j] = xr[c + j];
+                    const int cc = c < w0 ? c : w0 - 8;
+                    v = *(const h8 *)((const _Float16 *)a.x + rr * w0 + cc);
+                    v = (live && c < w0) ? v : (h8)(_Float16)0;
                 }
-                B[kb][t] = v;
+            } else {
+                const _Float16 *xr = (const _Float16 *)a.x + rr * a.w0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int cj = c + j;
+                    const _Float16 e = xr[cj < a.w0 ? cj : a.w0 - 1];
+                    v[j] = (live && cj < a.w0) ? e : (_Float16)0;
+                }
+            }
+            B[kb][t] = v;
+        }
+    }
+
+    template <int... T>
+    static __device__ __forceinline__ void load_inputs(h8 (&B)[N::KB(0)][NT], const LaunchArgs &a, int64_t row0,
+                                                       int lane, std::integer_sequence<int, T...>)
+    {
+        (load_tile<T>(B, a, row0, lane), ...);
+    }
+
+    // ---- last layer: FP32 -> FP16 and store -------------------------------------------------
+
+    template <int t>
+    static __device__ __forceinline__ void store_tile(const f4 (&acc)[NT], int mt, const LaunchArgs &a,
+                                                      int64_t row0, int lane)
+    {
+        const int g = lane >> 4, n = lane & 15;
+        const int c = 16 * mt + 4 * g;  // first output feature this lane holds
+        const h4 v = __builtin_convertvector(acc[t], h4);
+        const int64_t row = row0 + 16 * t + n;
+        if (row < a.batch) {
+            if constexpr (kVecOut) {
+                constexpr int wl = N::w[L];
+                if (c < wl)
+                    *(h4 *)((_Float16 *)a.y + row * wl + c) = v;
+            } else {
+                _Float16 *yr = (_Float16 *)a.y + row * a.wL;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (c + i < a.wL)
+                        yr[c + i] = v[i];
             }
         }
+    }
+
+    template <int... T>
+    static __device__ __forceinline__ void store_outputs(const f4 (&acc)[NT], int mt, const LaunchArgs &a,
+                                                         int64_t row0, int lane, std::integer_sequence<int, T...>)
+    {
+        (store_tile<T>(acc, mt, a, row0, lane), ...);
     }
 };
 
@@ -291,7 +325,7 @@ __global__ void __launch_bounds__(WAVES * 64) mlp_fused(LaunchArgs a)
         asm volatile("" ::: "memory");
         const int64_t row0 = tile * kRows;
         h8 B0[N::KB(0)][NT];
-        B::load_inputs(B0, a, row0, lane);
+        B::load_inputs(B0, a, row0, lane, std::make_integer_sequence<int, NT>());
         B::template layer<0>(src, B0, a, row0, lane);
     }
 }
