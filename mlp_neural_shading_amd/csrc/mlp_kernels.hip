@@ -81,6 +81,18 @@ struct BufferSource {  // image read through the caches with buffer loads (const
 // Buffer descriptor word 3 for gfx9-family raw buffers (32-bit data format, no swizzle).
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// Wave priority from progress: 3 for a wave on its first tile, then 2, 1, 0.
+__device__ __forceinline__ void set_priority(int it)
+{
+    switch (it) {
+    case 0: __builtin_amdgcn_s_setprio(3); break;
+    case 1: __builtin_amdgcn_s_setprio(2); break;
+    case 2: __builtin_amdgcn_s_setprio(1); break;
+    case 3: __builtin_amdgcn_s_setprio(0); break;
+    default: break;
+    }
+}
+
 // Compile-time description of the network a kernel instance computes.
 template <int... W>
 struct Net {
@@ -297,13 +309,26 @@ struct Body {
     }
 };
 
-template <class N, int NT, int WAVES, bool LDS_W, int LAYOUT, int ACT, bool GENERIC>
-__global__ void __launch_bounds__(WAVES * 64) mlp_fused(LaunchArgs a)
+// EU: waves per SIMD the instance is built for (its register budget is 512 / EU per lane).
+template <class N, int NT, int WAVES, int EU, bool LDS_W, int LAYOUT, int ACT, bool GENERIC>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(EU, EU))) mlp_fused(LaunchArgs a)
 {
     using Src = typename std::conditional<LDS_W, LdsSource, BufferSource>::type;
     using B = Body<N, NT, LAYOUT, ACT, GENERIC, LDS_W, Src>;
     constexpr int bytes = (int)N::image_bytes(LAYOUT);
     static_assert(bytes % 16 == 0, "image must be a multiple of 16 bytes");
+    constexpr int kRows = NT * 16;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tiles = (a.batch + kRows - 1) / kRows;
+    const int64_t stride = (int64_t)gridDim.x * WAVES;
+    int64_t tile = (int64_t)blockIdx.x * WAVES + wave;
+
+    // The first tile's inputs are requested before the weights are staged, so the two latencies
+    // overlap; every later tile's inputs are requested one tile ahead.
+    h8 Bnext[N::KB(0)][NT];
+    B::load_inputs(Bnext, a, (tile < tiles ? tile : 0) * kRows, lane, std::make_integer_sequence<int, NT>());
+
     Src src;
     if constexpr (LDS_W) {
         __shared__ __attribute__((aligned(16))) uint8_t lds[bytes];
@@ -314,30 +339,39 @@ __global__ void __launch_bounds__(WAVES * 64) mlp_fused(LaunchArgs a)
     } else {
         src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.image, 0, bytes, kBufferRsrcWord3);
     }
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    constexpr int kRows = NT * 16;
-    const int64_t tiles = (a.batch + kRows - 1) / kRows;
-    for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < tiles; tile += (int64_t)gridDim.x * WAVES) {
+
+    for (int it = 0; tile < tiles; tile += stride, ++it) {
+        // Waves of a SIMD start together and the oldest one is issued first; left alone, some
+        // race ahead and the last ones finish with nothing to overlap.  Giving the waves that are
+        // behind the higher priority keeps them in step.
+        set_priority(it);
         // The weights are loop-invariant; without this barrier the compiler hoists every fragment
         // read out of the tile loop and the whole image (up to ~1 KB per lane) spills.  The barrier
         // keeps them as per-tile reads, each reused across the NT sample tiles.
         asm volatile("" ::: "memory");
-        const int64_t row0 = tile * kRows;
-        h8 B0[N::KB(0)][NT];
-        B::load_inputs(B0, a, row0, lane, std::make_integer_sequence<int, NT>());
-        B::template layer<0>(src, B0, a, row0, lane);
+        constexpr int KB0 = N::KB(0);  // a constant expression, so the copy below fully unrolls
+        h8 B0[KB0][NT];
+#pragma unroll
+        for (int kb = 0; kb < KB0; ++kb)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                B0[kb][t] = Bnext[kb][t];
+        const int64_t next = tile + stride;
+        if (next < tiles)
+            B::load_inputs(Bnext, a, next * kRows, lane, std::make_integer_sequence<int, NT>());
+        B::template layer<0>(src, B0, a, tile * kRows, lane);
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
-template <class N, int NT, int WAVES, bool LDS_W, int LAYOUT, int ACT, bool GENERIC>
+template <class N, int NT, int WAVES, int EU, bool LDS_W, int LAYOUT, int ACT, bool GENERIC>
 hipError_t launch(const LaunchArgs &a, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((mlp_fused<N, NT, WAVES, LDS_W, LAYOUT, ACT, GENERIC>), dim3(grid), dim3(WAVES * 64), 0, s, a);
+    hipLaunchKernelGGL((mlp_fused<N, NT, WAVES, EU, LDS_W, LAYOUT, ACT, GENERIC>), dim3(grid), dim3(WAVES * 64), 0, s, a);
     return hipGetLastError();
 }
 
-template <class N, int NT, int WAVES, bool LDS_W, int LAYOUT, int ACT, bool GENERIC>
+template <class N, int NT, int WAVES, int EU, bool LDS_W, int LAYOUT, int ACT, bool GENERIC>
 KernelEntry entry(const char *name)
 {
     KernelEntry e{};
@@ -351,8 +385,8 @@ KernelEntry entry(const char *name)
     e.threads = WAVES * 64;
     e.rows_per_wave = NT * 16;
     e.weights_in_lds = LDS_W;
-    e.launch = &launch<N, NT, WAVES, LDS_W, LAYOUT, ACT, GENERIC>;
-    e.func = (const void *)&mlp_fused<N, NT, WAVES, LDS_W, LAYOUT, ACT, GENERIC>;
+    e.launch = &launch<N, NT, WAVES, EU, LDS_W, LAYOUT, ACT, GENERIC>;
+    e.func = (const void *)&mlp_fused<N, NT, WAVES, EU, LDS_W, LAYOUT, ACT, GENERIC>;
     return e;
 }
 
@@ -364,20 +398,21 @@ using NetHetero = Net<32, 64, 64, 64, 128, 64, 64, 32, 4>;
 using NetWide = Net<64, 128, 128, 128, 128, 128, 128, 128, 4>;
 using NetStream = Net<64, 64, 64, 64, 64, 64, 64, 64, 16>;
 
-#define MLP_VARIANTS(NET, NT, WAVES, LDS, TAG)                                                              \
-    entry<NET, NT, WAVES, LDS, kPacked, kVector, false>("mlp_fused<" TAG ",packed,vector>"),               \
-        entry<NET, NT, WAVES, LDS, kPacked, kScalarised, false>("mlp_fused<" TAG ",packed,scalarised>"),   \
-        entry<NET, NT, WAVES, LDS, kRowMajor, kVector, false>("mlp_fused<" TAG ",rowmajor,vector>"),       \
-        entry<NET, NT, WAVES, LDS, kRowMajor, kScalarised, false>("mlp_fused<" TAG ",rowmajor,scalarised>")
+#define MLP_VARIANTS(NET, NT, WAVES, EU, LDS, TAG)                                                             \
+    entry<NET, NT, WAVES, EU, LDS, kPacked, kVector, false>("mlp_fused<" TAG ",packed,vector>"),                  \
+        entry<NET, NT, WAVES, EU, LDS, kPacked, kScalarised, false>("mlp_fused<" TAG ",packed,scalarised>"),      \
+        entry<NET, NT, WAVES, EU, LDS, kRowMajor, kVector, false>("mlp_fused<" TAG ",rowmajor,vector>"),          \
+        entry<NET, NT, WAVES, EU, LDS, kRowMajor, kScalarised, false>("mlp_fused<" TAG ",rowmajor,scalarised>")
 
-#define MLP_GENERIC(...) entry<Net<__VA_ARGS__>, 1, 4, false, kPacked, kVector, true>
+#define MLP_GENERIC(...) entry<Net<__VA_ARGS__>, 1, 4, 2, false, kPacked, kVector, true>
 
 static const KernelEntry kEntries[] = {
-    MLP_VARIANTS(NetSmall, 4, 8, true, "16-32x7-4"),
-    MLP_VARIANTS(NetPage, 4, 8, true, "32-64x7-4"),
-    MLP_VARIANTS(NetHetero, 4, 8, true, "32-64-64-64-128-64-64-32-4"),
-    MLP_VARIANTS(NetWide, 4, 4, false, "64-128x7-4"),
-    MLP_VARIANTS(NetStream, 4, 8, true, "64-64x7-16"),
+    // (net, rows tiles per wave, waves per workgroup, waves per SIMD, image in LDS)
+    MLP_VARIANTS(NetSmall, 4, 8, 4, true, "16-32x7-4"),
+    MLP_VARIANTS(NetPage, 4, 8, 4, true, "32-64x7-4"),
+    MLP_VARIANTS(NetHetero, 4, 8, 4, true, "32-64-64-64-128-64-64-32-4"),
+    MLP_VARIANTS(NetWide, 4, 4, 1, false, "64-128x7-4"),
+    MLP_VARIANTS(NetStream, 4, 8, 4, true, "64-64x7-16"),
     MLP_GENERIC(128, 128)("mlp_fused<generic128,L=1>"),
     MLP_GENERIC(128, 128, 128)("mlp_fused<generic128,L=2>"),
     MLP_GENERIC(128, 128, 128, 128)("mlp_fused<generic128,L=3>"),
