@@ -22,6 +22,9 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # no packed-FP32 instructions anywhere (hipcc's host pass warns that it does not know the feature)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a single-lane LDS atomic claims the next tile and its result is read an iteration later; the
+    # wave-aggregating rewrite of atomics would consume the result at once and stall the wave
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 SOURCES = ["mlp_kernels.hip", "mlp_api.cpp", "mlp_pack.cpp"]
 

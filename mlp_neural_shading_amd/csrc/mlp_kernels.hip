@@ -6,8 +6,11 @@
 //   - the weight image is staged once per workgroup into LDS (or, when it does not fit in LDS, read
 //     through the caches), and every A fragment is one 16-byte read per lane reused across the
 //     wave's NT sample tiles;
-//   - each layer is v_mfma_f32_16x16x32_f16 with the bias as the C operand of the first K block
-//     (FP16 x FP16 products, FP32 accumulation);
+//   - each layer is v_mfma_f32_32x32x16_f16 with the bias as the C operand of the first K block
+//     (FP16 x FP16 products, FP32 accumulation).  The 32x32 shape does twice the work of the
+//     16x16x32 one per issued instruction, which leaves the VALU room for the epilogue: measured on
+//     MI355X, about six packed-FP16 VALU instructions fit under each 32x32x16 MFMA at no cost, while
+//     more than two per 16x16x32 MFMA already slow the MFMA pipe;
 //   - the epilogue of layers 1..L-1 converts FP32 -> FP16 with round-to-nearest-even and applies the
 //     leaky ReLU max(v, v * half(0.01)) as packed FP16 operations on whole registers, the vector form
 //     of "Bad versus good activation"; by the slot order in mlp_layout.h the result already sits
@@ -29,24 +32,26 @@ namespace mlpk {
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f8 __attribute__((ext_vector_type(8)));
+typedef float f16x __attribute__((ext_vector_type(16)));
 
 // half(0.01): 0.01 rounded to binary16 (0x211f = 0.01000213623046875).
 __device__ __forceinline__ _Float16 slope() { return __builtin_bit_cast(_Float16, (unsigned short)0x211f); }
 
-__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+__device__ __forceinline__ f16x mfma(h8 a, h8 b, f16x c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
 
-// Vector leaky ReLU on four FP16 values: two packed instructions for every two values.
-__device__ __forceinline__ h4 leaky_vector(h4 v)
+// Vector leaky ReLU on eight FP16 values: two packed instructions for every two values.
+__device__ __forceinline__ h8 leaky_vector(h8 v)
 {
-    const h4 s = (h4)slope();
+    const h8 s = (h8)slope();
     return __builtin_elementwise_max(v, v * s);
 }
 
 // Scalarised leaky ReLU: each component on its own, with a compare and a conditional multiply.
-__device__ __forceinline__ h4 leaky_scalarised(h4 v)
+__device__ __forceinline__ h8 leaky_scalarised(h8 v)
 {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 8; ++c) {
         _Float16 e = v[c];
         // The empty asm pins each element as a separate scalar value so that the compiler cannot
         // re-vectorise the loop into the packed form.
@@ -81,18 +86,6 @@ struct BufferSource {  // image read through the caches with buffer loads (const
 // Buffer descriptor word 3 for gfx9-family raw buffers (32-bit data format, no swizzle).
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
-// Wave priority from progress: 3 for a wave on its first tile, then 2, 1, 0.
-__device__ __forceinline__ void set_priority(int it)
-{
-    switch (it) {
-    case 0: __builtin_amdgcn_s_setprio(3); break;
-    case 1: __builtin_amdgcn_s_setprio(2); break;
-    case 2: __builtin_amdgcn_s_setprio(1); break;
-    case 3: __builtin_amdgcn_s_setprio(0); break;
-    default: break;
-    }
-}
-
 // Compile-time description of the network a kernel instance computes.
 template <int... W>
 struct Net {
@@ -119,25 +112,24 @@ struct Body {
         if constexpr (LAYOUT == kPacked) {
             return src.load16(lane * 16, (int)mlpl::pk_a_off(N::w, l) + (mt * KB + kb) * mlpl::kFragBytes);
         } else {
-            // Row-major [out][in]: lane (g, m) gathers row 16 mt + m at its slot features.
+            // Row-major [out][in]: lane (g, m) gathers row 32 mt + m at its slot features.
             constexpr int win = N::w[l], wout = N::w[l + 1];
             static_assert(l > 0 || win % 8 == 0, "row-major input layer needs w0 % 8 == 0");
             static_assert(l == 0 || win % 4 == 0, "row-major hidden layer needs w % 4 == 0");
-            const int g = lane >> 4, m = lane & 15;
-            const int r = 16 * mt + m;
-            const int row = (int)mlpl::rm_w_off(N::w, l) + 16 * mt * win * 2;  // wave-uniform
+            const int g = lane >> 5, m = lane & 31;
+            const int r = 32 * mt + m;
+            const int row = (int)mlpl::rm_w_off(N::w, l) + 32 * mt * win * 2;  // wave-uniform
             h8 a = (h8)(_Float16)0;
             if constexpr (l == 0) {
-                const int f = 32 * kb + 8 * g;
-                if (r < wout && f < win)
-                    a = src.load16((m * win + 8 * g) * 2, row + 32 * kb * 2);
+                if (r < wout && 16 * kb + 8 * g < win)
+                    a = src.load16((m * win + 8 * g) * 2, row + 16 * kb * 2);
             } else {
-                const int f0 = 32 * kb + 4 * g, f1 = f0 + 16;
+                const int f0 = 16 * kb + 4 * g, f1 = f0 + 8;
                 h4 lo = (h4)(_Float16)0, hi = (h4)(_Float16)0;
                 if (r < wout && f0 < win)
-                    lo = src.load8((m * win + 4 * g) * 2, row + 32 * kb * 2);
+                    lo = src.load8((m * win + 4 * g) * 2, row + 16 * kb * 2);
                 if (r < wout && f1 < win)
-                    hi = src.load8((m * win + 4 * g) * 2, row + (32 * kb + 16) * 2);
+                    hi = src.load8((m * win + 4 * g) * 2, row + (16 * kb + 8) * 2);
                 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
             return a;
@@ -145,22 +137,85 @@ struct Body {
     }
 
     template <int l>
-    static __device__ __forceinline__ f4 bias_tile(const Src &src, int mt, int lane)
+    static __device__ __forceinline__ f16x bias_tile(const Src &src, int mt, int lane)
     {
-        const int g = lane >> 4;
+        const int g = lane >> 5;
         if constexpr (LAYOUT == kPacked) {
-            return __builtin_bit_cast(f4, src.load16(g * 16, (int)mlpl::pk_b_off(N::w, l) + mt * mlpl::kBiasTileBytes));
+            const int soff = (int)mlpl::pk_b_off(N::w, l) + mt * mlpl::kBiasTileBytes;
+            const f4 b0 = __builtin_bit_cast(f4, src.load16(g * 64, soff));
+            const f4 b1 = __builtin_bit_cast(f4, src.load16(g * 64 + 16, soff));
+            const f4 b2 = __builtin_bit_cast(f4, src.load16(g * 64 + 32, soff));
+            const f4 b3 = __builtin_bit_cast(f4, src.load16(g * 64 + 48, soff));
+            const f8 lo = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+            const f8 hi = __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7);
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
         } else {
             constexpr int wout = N::w[l + 1];
             static_assert(wout % 4 == 0, "row-major layer needs w_out % 4 == 0");
-            h4 b = (h4)(_Float16)0;
-            if (16 * mt + 4 * g < wout)
-                b = src.load8(g * 8, (int)mlpl::rm_b_off(N::w, l) + 16 * mt * 2);
-            return __builtin_convertvector(b, f4);
+            const int soff = (int)mlpl::rm_b_off(N::w, l) + 32 * mt * 2;
+            h4 q[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                q[k] = (h4)(_Float16)0;
+                if (32 * mt + 8 * k + 4 * g < wout)
+                    q[k] = src.load8((8 * k + 4 * g) * 2, soff);
+            }
+            const h8 lo = __builtin_shufflevector(q[0], q[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const h8 hi = __builtin_shufflevector(q[2], q[3], 0, 1, 2, 3, 4, 5, 6, 7);
+            return __builtin_convertvector(
+                __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15), f16x);
         }
     }
 
     // ---- one layer: NT sample tiles x MT output tiles x KB input blocks --------------------
+    //
+    // Software-pipelined over the output tiles mt: the fragments of tile mt+1 are requested first,
+    // then tile mt's MFMAs are issued, then tile mt-1's epilogue runs.  The epilogue does not depend
+    // on the MFMAs in flight, so the MFMA pipe and the VALU work side by side.
+
+    template <int l>
+    static __device__ __forceinline__ void fetch(const Src &src, int mt, h8 (&af)[N::KB(l)], f16x &bias, int lane)
+    {
+        constexpr int KB = N::KB(l);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            af[kb] = a_frag<l>(src, mt, kb, lane);
+        bias = bias_tile<l>(src, mt, lane);
+    }
+
+    template <int l>
+    static __device__ __forceinline__ void mfmas(const h8 (&af)[N::KB(l)], const h8 (&Bin)[N::KB(l)][NT],
+                                                 const f16x &bias, f16x (&acc)[NT])
+    {
+        constexpr int KB = N::KB(l);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = mfma(af[0], Bin[0][t], bias);
+#pragma unroll
+        for (int kb = 1; kb < KB; ++kb)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = mfma(af[kb], Bin[kb][t], acc[t]);
+    }
+
+    // FP32 -> FP16 (round to nearest even) and leaky ReLU of output tile mt; accumulator half h of
+    // each lane is exactly block 2 mt + h of the next layer's B operand (see mlp_layout.h).
+    template <int KBN>
+    static __device__ __forceinline__ void epilogue(int mt, const f16x (&acc)[NT], h8 (&Bout)[KBN][NT])
+    {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (2 * mt + h < KBN) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const f8 half = h == 0 ? __builtin_shufflevector(acc[t], acc[t], 0, 1, 2, 3, 4, 5, 6, 7)
+                                           : __builtin_shufflevector(acc[t], acc[t], 8, 9, 10, 11, 12, 13, 14, 15);
+                    const h8 v = __builtin_convertvector(half, h8);  // v_cvt_pk_f16_f32: nearest even
+                    Bout[2 * mt + h][t] = (ACT == kVector) ? leaky_vector(v) : leaky_scalarised(v);
+                }
+            }
+        }
+    }
 
     template <int l>
     static __device__ __forceinline__ void layer(const Src &wb, const h8 (&Bin)[N::KB(l)][NT],
@@ -171,145 +226,184 @@ struct Body {
         // scheduler front-loads the whole network's fragments and runs out of registers.
         if constexpr (!LDS_W)
             asm volatile("" ::: "memory");
+        h8 af[KB];
+        f16x bias;
+        fetch<l>(wb, 0, af, bias, lane);
         if constexpr (l + 1 < L) {
-            h8 Bout[N::KB(l + 1)][NT];
-            h4 pend[NT];
+            constexpr int KBN = N::KB(l + 1);
+            h8 Bout[KBN][NT];
+            f16x prev[NT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                h8 af[KB];
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    af[kb] = a_frag<l>(wb, mt, kb, lane);
-                const f4 bias = bias_tile<l>(wb, mt, lane);
-                f4 acc[NT];
+                h8 afn[KB];
+                f16x biasn;
+                if (mt + 1 < MT)
+                    fetch<l>(wb, mt + 1, afn, biasn, lane);
+                f16x acc[NT];
+                mfmas<l>(af, Bin, bias, acc);
+                if (mt > 0)
+                    epilogue<KBN>(mt - 1, prev, Bout);
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-                    acc[t] = mfma(af[0], Bin[0][t], bias);
+                    prev[t] = acc[t];
+                if (mt + 1 < MT) {
 #pragma unroll
-                for (int kb = 1; kb < KB; ++kb)
-#pragma unroll
-                    for (int t = 0; t < NT; ++t)
-                        acc[t] = mfma(af[kb], Bin[kb][t], acc[t]);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    h4 v = __builtin_convertvector(acc[t], h4);  // v_cvt_pk_f16_f32: round to nearest even
-                    v = (ACT == kVector) ? leaky_vector(v) : leaky_scalarised(v);
-                    if (mt % 2 == 0) {
-                        pend[t] = v;
-                        if (mt == MT - 1)
-                            Bout[mt / 2][t] = __builtin_shufflevector(v, (h4)(_Float16)0, 0, 1, 2, 3, 4, 5, 6, 7);
-                    } else {
-                        Bout[mt / 2][t] = __builtin_shufflevector(pend[t], v, 0, 1, 2, 3, 4, 5, 6, 7);
-                    }
+                    for (int kb = 0; kb < KB; ++kb)
+                        af[kb] = afn[kb];
+                    bias = biasn;
                 }
             }
+            epilogue<KBN>(MT - 1, prev, Bout);
             layer<l + 1>(wb, Bout, a, row0, lane);
         } else {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                h8 af[KB];
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    af[kb] = a_frag<l>(wb, mt, kb, lane);
-                const f4 bias = bias_tile<l>(wb, mt, lane);
-                f4 acc[NT];
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    acc[t] = mfma(af[0], Bin[0][t], bias);
-#pragma unroll
-                for (int kb = 1; kb < KB; ++kb)
-#pragma unroll
-                    for (int t = 0; t < NT; ++t)
-                        acc[t] = mfma(af[kb], Bin[kb][t], acc[t]);
+                h8 afn[KB];
+                f16x biasn;
+                if (mt + 1 < MT)
+                    fetch<l>(wb, mt + 1, afn, biasn, lane);
+                f16x acc[NT];
+                mfmas<l>(af, Bin, bias, acc);
                 store_outputs(acc, mt, a, row0, lane, std::make_integer_sequence<int, NT>());
+                if (mt + 1 < MT) {
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+                        af[kb] = afn[kb];
+                    bias = biasn;
+                }
             }
         }
     }
 
     // ---- input rows -> layer-0 B fragments --------------------------------------------------
     //
-    // Written as one straight-line body per sample tile (an index-sequence expansion, not a loop):
-    // a loop over tiles with the "row < batch" test gets peeled by the compiler into a run-time loop
-    // with dynamically indexed fragment registers.  Loads are branch-free: the address is clamped to
-    // a valid row and the value replaced by zero for rows past the batch.
+    // Loads are issued one tile ahead and must not be waited for until the tile is used, so they
+    // are raw (address clamped to a valid row and column, no select on the value: a select right
+    // after the load would make the wave wait for it).  Rows past the batch and columns past w0 are
+    // zeroed when the fragments are consumed.  Everything is written as one straight-line body per
+    // sample tile (an index-sequence expansion) with constant-expression loop bounds, so the
+    // fragment arrays stay in registers.
 
     template <int t>
-    static __device__ __forceinline__ void load_tile(h8 (&B)[N::KB(0)][NT], const LaunchArgs &a, int64_t row0,
+    static __device__ __forceinline__ void load_tile(h8 (&R)[N::KB(0)][NT], const LaunchArgs &a, int64_t row0,
                                                      int lane)
     {
-        const int g = lane >> 4, n = lane & 15;
-        const int64_t row = row0 + 16 * t + n;
-        const bool live = row < a.batch;
-        const int64_t rr = live ? row : a.batch - 1;
-        constexpr int KB0 = N::KB(0);  // a constant expression, so the loop below fully unrolls
+        const int g = lane >> 5, n = lane & 31;
+        const int64_t row = row0 + 32 * t + n;
+        const int64_t rr = row < a.batch ? row : a.batch - 1;
+        constexpr int KB0 = N::KB(0);
 #pragma unroll
         for (int kb = 0; kb < KB0; ++kb) {
-            const int c = 32 * kb + 8 * g;
-            h8 v = (h8)(_Float16)0;  // padded slots are zero in registers, never loaded
+            const int c = 16 * kb + 8 * g;
             if constexpr (kVecIn) {
                 constexpr int w0 = N::w[0];
-                if (32 * kb + 32 <= w0) {  // whole block inside the row (folds after unrolling)
-                    v = *(const h8 *)((const _Float16 *)a.x + rr * w0 + c);
-                    v = live ? v : (h8)(_Float16)0;
-                } else {
-                    const int cc = c < w0 ? c : w0 - 8;
-                    v = *(const h8 *)((const _Float16 *)a.x + rr * w0 + cc);
-                    v = (live && c < w0) ? v : (h8)(_Float16)0;
-                }
+                const int cc = (16 * kb + 16 <= w0 || c < w0) ? c : w0 - 8;  // folds for whole blocks
+                R[kb][t] = *(const h8 *)((const _Float16 *)a.x + rr * w0 + cc);
             } else {
                 const _Float16 *xr = (const _Float16 *)a.x + rr * a.w0;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int cj = c + j;
-                    const _Float16 e = xr[cj < a.w0 ? cj : a.w0 - 1];
-                    v[j] = (live && cj < a.w0) ? e : (_Float16)0;
-                }
+                for (int j = 0; j < 8; ++j)
+                    R[kb][t][j] = xr[c + j < a.w0 ? c + j : a.w0 - 1];
             }
-            B[kb][t] = v;
         }
     }
 
     template <int... T>
-    static __device__ __forceinline__ void load_inputs(h8 (&B)[N::KB(0)][NT], const LaunchArgs &a, int64_t row0,
+    static __device__ __forceinline__ void load_inputs(h8 (&R)[N::KB(0)][NT], const LaunchArgs &a, int64_t row0,
                                                        int lane, std::integer_sequence<int, T...>)
     {
-        (load_tile<T>(B, a, row0, lane), ...);
+        (load_tile<T>(R, a, row0, lane), ...);
+    }
+
+    // B = R with the padded slots (columns >= w0) and the rows past the batch set to zero.
+    template <int t>
+    static __device__ __forceinline__ void mask_tile(h8 (&B)[N::KB(0)][NT], const h8 (&R)[N::KB(0)][NT],
+                                                     const LaunchArgs &a, int64_t row0, int lane)
+    {
+        const int g = lane >> 5, n = lane & 31;
+        const bool live = row0 + 32 * t + n < a.batch;
+        constexpr int KB0 = N::KB(0);
+#pragma unroll
+        for (int kb = 0; kb < KB0; ++kb) {
+            const int c = 16 * kb + 8 * g;
+            if constexpr (kVecIn) {
+                constexpr int w0 = N::w[0];
+                const bool in = 16 * kb + 16 <= w0 || c < w0;  // folds for whole blocks
+                B[kb][t] = (live && in) ? R[kb][t] : (h8)(_Float16)0;
+            } else {
+                h8 v = R[kb][t];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v[j] = (live && c + j < a.w0) ? v[j] : (_Float16)0;
+                B[kb][t] = v;
+            }
+        }
+    }
+
+    template <int... T>
+    static __device__ __forceinline__ void mask_inputs(h8 (&B)[N::KB(0)][NT], const h8 (&R)[N::KB(0)][NT],
+                                                       const LaunchArgs &a, int64_t row0, int lane,
+                                                       std::integer_sequence<int, T...>)
+    {
+        (mask_tile<T>(B, R, a, row0, lane), ...);
     }
 
     // ---- last layer: FP32 -> FP16 and store -------------------------------------------------
 
     template <int t>
-    static __device__ __forceinline__ void store_tile(const f4 (&acc)[NT], int mt, const LaunchArgs &a,
+    static __device__ __forceinline__ void store_tile(const f16x (&acc)[NT], int mt, const LaunchArgs &a,
                                                       int64_t row0, int lane)
     {
-        const int g = lane >> 4, n = lane & 15;
-        const int c = 16 * mt + 4 * g;  // first output feature this lane holds
-        const h4 v = __builtin_convertvector(acc[t], h4);
-        const int64_t row = row0 + 16 * t + n;
+        const int g = lane >> 5, n = lane & 31;
+        const int64_t row = row0 + 32 * t + n;
         if (row < a.batch) {
-            if constexpr (kVecOut) {
-                constexpr int wl = N::w[L];
-                if (c < wl)
-                    *(h4 *)((_Float16 *)a.y + row * wl + c) = v;
-            } else {
-                _Float16 *yr = (_Float16 *)a.y + row * a.wL;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (c + i < a.wL)
-                        yr[c + i] = v[i];
+            for (int q = 0; q < 4; ++q) {
+                const int c = 32 * mt + 8 * q + 4 * g;  // first of the 4 outputs held by this lane
+                const f4 part = {acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
+                if constexpr (kVecOut) {
+                    constexpr int wl = N::w[L];
+                    if (32 * mt + 8 * q < wl && c < wl)
+                        *(h4 *)((_Float16 *)a.y + row * wl + c) = __builtin_convertvector(part, h4);
+                } else {
+                    _Float16 *yr = (_Float16 *)a.y + row * a.wL;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (c + i < a.wL)
+                            yr[c + i] = (_Float16)part[i];
+                }
             }
         }
     }
 
     template <int... T>
-    static __device__ __forceinline__ void store_outputs(const f4 (&acc)[NT], int mt, const LaunchArgs &a,
+    static __device__ __forceinline__ void store_outputs(const f16x (&acc)[NT], int mt, const LaunchArgs &a,
                                                          int64_t row0, int lane, std::integer_sequence<int, T...>)
     {
         (store_tile<T>(acc, mt, a, row0, lane), ...);
     }
 };
 
+// Copy the weight image into LDS with every load in flight before the first store (the copy is a
+// handful of 16-byte loads per thread, so its cost is one round trip rather than one per load).
+// Written as an index-sequence expansion with constant indices: a loop-indexed staging array would
+// be placed in LDS by the compiler.  Load addresses are clamped into the image; only in-range
+// chunks are stored.
+template <int BYTES, int THREADS, int... K>
+__device__ __forceinline__ void stage_image(uint8_t *lds, const uint8_t *image, std::integer_sequence<int, K...>)
+{
+    const int t16 = (int)threadIdx.x * 16;
+    const uint4 v[] = {*(const uint4 *)(image + (K * THREADS * 16 + t16 < BYTES ? K * THREADS * 16 + t16 : BYTES - 16))...};
+    ((K * THREADS * 16 + t16 < BYTES ? (void)(*(uint4 *)(lds + K * THREADS * 16 + t16) = v[K]) : (void)0), ...);
+}
+
 // EU: waves per SIMD the instance is built for (its register budget is 512 / EU per lane).
+//
+// Work distribution: workgroup b owns the contiguous tiles [lo, hi) of an even split; its waves take
+// the first WAVES of them and then claim the next unclaimed tile from a counter in LDS.  The waves
+// sharing a SIMD are not issued fairly (the oldest goes first), so with a fixed share per wave one of
+// them finishes well before the other and the SIMD runs the rest half-empty; claiming tiles keeps
+// every wave busy until the range is exhausted.
 template <class N, int NT, int WAVES, int EU, bool LDS_W, int LAYOUT, int ACT, bool GENERIC>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(EU, EU))) mlp_fused(LaunchArgs a)
 {
@@ -317,51 +411,65 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
     using B = Body<N, NT, LAYOUT, ACT, GENERIC, LDS_W, Src>;
     constexpr int bytes = (int)N::image_bytes(LAYOUT);
     static_assert(bytes % 16 == 0, "image must be a multiple of 16 bytes");
-    constexpr int kRows = NT * 16;
+    constexpr int kRows = NT * 32;
+    __shared__ int next_tile;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t tiles = (a.batch + kRows - 1) / kRows;
-    const int64_t stride = (int64_t)gridDim.x * WAVES;
-    int64_t tile = (int64_t)blockIdx.x * WAVES + wave;
+    const int64_t lo = (int64_t)blockIdx.x * tiles / gridDim.x;
+    const int64_t hi = ((int64_t)blockIdx.x + 1) * tiles / gridDim.x;
+    // Each wave starts with two tiles of its own; later tiles are claimed two ahead, so neither the
+    // claim's result nor a tile's inputs are waited for in the iteration that requests them.
+    int64_t tile = lo + wave;
+    int64_t next = lo + WAVES + wave;
 
     // The first tile's inputs are requested before the weights are staged, so the two latencies
     // overlap; every later tile's inputs are requested one tile ahead.
-    h8 Bnext[N::KB(0)][NT];
-    B::load_inputs(Bnext, a, (tile < tiles ? tile : 0) * kRows, lane, std::make_integer_sequence<int, NT>());
+    constexpr int KB0 = N::KB(0);  // a constant expression, so the loops below fully unroll
+    h8 Bnext[KB0][NT];
+    B::load_inputs(Bnext, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
 
     Src src;
     if constexpr (LDS_W) {
         __shared__ __attribute__((aligned(16))) uint8_t lds[bytes];
-        for (int i = threadIdx.x * 16; i < bytes; i += WAVES * 64 * 16)
-            *(uint4 *)(lds + i) = *(const uint4 *)(a.image + i);
-        __syncthreads();
+        constexpr int kChunks = (bytes + WAVES * 64 * 16 - 1) / (WAVES * 64 * 16);
+        stage_image<bytes, WAVES * 64>(lds, a.image, std::make_integer_sequence<int, kChunks>());
         src.base = lds;
     } else {
         src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.image, 0, bytes, kBufferRsrcWord3);
     }
+    if (threadIdx.x == 0)
+        next_tile = 2 * WAVES;  // tiles are counted from lo
+    __syncthreads();
 
-    for (int it = 0; tile < tiles; tile += stride, ++it) {
-        // Waves of a SIMD start together and the oldest one is issued first; left alone, some
-        // race ahead and the last ones finish with nothing to overlap.  Giving the waves that are
-        // behind the higher priority keeps them in step.
-        set_priority(it);
+    int claimed = 0;
+    if (lane == 0)
+        claimed = atomicAdd(&next_tile, 1);
+    while (tile < hi) {
         // The weights are loop-invariant; without this barrier the compiler hoists every fragment
         // read out of the tile loop and the whole image (up to ~1 KB per lane) spills.  The barrier
         // keeps them as per-tile reads, each reused across the NT sample tiles.
         asm volatile("" ::: "memory");
-        constexpr int KB0 = N::KB(0);  // a constant expression, so the copy below fully unrolls
         h8 B0[KB0][NT];
+        constexpr bool kWholeBlocks = B::kVecIn && N::w[0] % 16 == 0;
+        if (kWholeBlocks && (tile + 1) * kRows <= a.batch) {  // whole tile, whole blocks: no masking
 #pragma unroll
-        for (int kb = 0; kb < KB0; ++kb)
+            for (int kb = 0; kb < KB0; ++kb)
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                B0[kb][t] = Bnext[kb][t];
-        const int64_t next = tile + stride;
-        if (next < tiles)
+                for (int t = 0; t < NT; ++t)
+                    B0[kb][t] = Bnext[kb][t];
+        } else {
+            B::mask_inputs(B0, Bnext, a, tile * kRows, lane, std::make_integer_sequence<int, NT>());
+        }
+        if (next < hi)
             B::load_inputs(Bnext, a, next * kRows, lane, std::make_integer_sequence<int, NT>());
+        const int64_t after = lo + __builtin_amdgcn_readfirstlane(claimed);  // claimed one tile ago
+        if (lane == 0)
+            claimed = atomicAdd(&next_tile, 1);
         B::template layer<0>(src, B0, a, tile * kRows, lane);
+        tile = next;
+        next = after;
     }
-    __builtin_amdgcn_s_setprio(0);
 }
 
 template <class N, int NT, int WAVES, int EU, bool LDS_W, int LAYOUT, int ACT, bool GENERIC>
@@ -383,7 +491,7 @@ KernelEntry entry(const char *name)
     e.layout = LAYOUT;
     e.act = ACT;
     e.threads = WAVES * 64;
-    e.rows_per_wave = NT * 16;
+    e.rows_per_wave = NT * 32;
     e.weights_in_lds = LDS_W;
     e.launch = &launch<N, NT, WAVES, EU, LDS_W, LAYOUT, ACT, GENERIC>;
     e.func = (const void *)&mlp_fused<N, NT, WAVES, EU, LDS_W, LAYOUT, ACT, GENERIC>;
@@ -404,15 +512,15 @@ using NetStream = Net<64, 64, 64, 64, 64, 64, 64, 64, 16>;
         entry<NET, NT, WAVES, EU, LDS, kRowMajor, kVector, false>("mlp_fused<" TAG ",rowmajor,vector>"),          \
         entry<NET, NT, WAVES, EU, LDS, kRowMajor, kScalarised, false>("mlp_fused<" TAG ",rowmajor,scalarised>")
 
-#define MLP_GENERIC(...) entry<Net<__VA_ARGS__>, 1, 4, 2, false, kPacked, kVector, true>
+#define MLP_GENERIC(...) entry<Net<__VA_ARGS__>, 1, 4, 1, false, kPacked, kVector, true>
 
 static const KernelEntry kEntries[] = {
-    // (net, rows tiles per wave, waves per workgroup, waves per SIMD, image in LDS)
-    MLP_VARIANTS(NetSmall, 4, 8, 4, true, "16-32x7-4"),
-    MLP_VARIANTS(NetPage, 4, 8, 4, true, "32-64x7-4"),
-    MLP_VARIANTS(NetHetero, 4, 8, 4, true, "32-64-64-64-128-64-64-32-4"),
-    MLP_VARIANTS(NetWide, 4, 4, 1, false, "64-128x7-4"),
-    MLP_VARIANTS(NetStream, 4, 8, 4, true, "64-64x7-16"),
+    // (net, 32-row tiles per wave, waves per workgroup, waves per SIMD, image in LDS)
+    MLP_VARIANTS(NetSmall, 2, 8, 4, true, "16-32x7-4"),
+    MLP_VARIANTS(NetPage, 2, 8, 2, true, "32-64x7-4"),
+    MLP_VARIANTS(NetHetero, 2, 8, 2, true, "32-64-64-64-128-64-64-32-4"),
+    MLP_VARIANTS(NetWide, 2, 4, 1, false, "64-128x7-4"),
+    MLP_VARIANTS(NetStream, 2, 8, 2, true, "64-64x7-16"),
     MLP_GENERIC(128, 128)("mlp_fused<generic128,L=1>"),
     MLP_GENERIC(128, 128, 128)("mlp_fused<generic128,L=2>"),
     MLP_GENERIC(128, 128, 128, 128)("mlp_fused<generic128,L=3>"),

@@ -1,24 +1,26 @@
 // mlp_layout.h -- geometry of the device weight images, shared by the host packer and the kernels.
 //
-// Tiling.  Every layer runs as v_mfma_f32_16x16x32_f16 with the weights in the A operand (16 output
-// features x 32 input features per fragment), the samples in the B operand (32 input features x 16
-// samples) and the 16x16 FP32 result in D.  Lane l of a wave is (g, n) = (l / 16, l % 16):
+// Tiling.  Every layer runs as v_mfma_f32_32x32x16_f16 with the weights in the A operand (32 output
+// features x 16 input features per fragment), the samples in the B operand (16 input features x 32
+// samples) and the 32x32 FP32 result in D.  Lane l of a wave is (g, n) = (l / 32, l % 32):
 //   A fragment: lane (g, m) holds row m and the 8 input-feature "slots" of group g,
 //   B fragment: lane (g, n) holds sample n and the same 8 slots,
-//   D fragment: lane (g, n) holds output features 4g .. 4g+3 of sample n (in FP32).
+//   D fragment: lane (g, n) holds, for sample n, the 16 output features 8 q + 4 g + i (q, i in 0..3),
+//               as accumulator element j = 4 q + i.
 // Only the pairing of A's and B's slots matters to the product, so the slot -> feature map is ours
-// to choose, per layer:
-//   layer 0 (reads the caller's row-major input): slot (kb, g, j) = feature 32 kb + 8 g + j, so one
+// to choose, per layer; block kb always covers input features 16 kb .. 16 kb + 15:
+//   layer 0 (reads the caller's row-major input): slot (kb, g, j) = feature 16 kb + 8 g + j, so one
 //     16-byte load per lane fills a B fragment;
-//   layer l >= 1: slot (kb, g, j) = feature 16 (2 kb + j / 4) + 4 g + j % 4, which is exactly what lane
-//     (g, n) holds in D after the previous layer (output tiles 2 kb and 2 kb + 1).  The hand-off
-//     between layers is therefore an in-lane FP32 -> FP16 convert, with no data movement.
+//   layer l >= 1: slot (kb, g, j) = feature 16 kb + 8 (j / 4) + 4 g + j % 4.  Output tile mt of the
+//     previous layer feeds blocks 2 mt and 2 mt + 1, and accumulator elements 8 h .. 8 h + 7 of lane
+//     (g, n) are exactly slots 0..7 of block 2 mt + h in the same lane: the hand-off between layers
+//     is an in-lane FP32 -> FP16 convert of each half of the accumulator, with no data movement.
 // The packer applies this permutation to the weight columns once ("Row-major versus
 // InferencingOptimal weights": the optimal layout is a one-time reordering of the same matrices).
 //
-// Packed image, per layer l (MT = output tiles of 16, KB = input blocks of 32):
+// Packed image, per layer l (MT = output tiles of 32, KB = input blocks of 16):
 //   A fragments  [mt][kb][lane][8 halves]   1024 bytes per fragment, one ds_read_b128 per lane
-//   bias tiles   [mt][g][4 floats]          FP32, lane (g, n) reads b[16 mt + 4 g .. + 3]
+//   bias tiles   [mt][g][16 floats]         FP32, lane (g, n) reads b[32 mt + 8 q + 4 g + i]
 // Row-major image, per layer l: W_l [w_out][w_in] FP16 as given, then b_l [w_out] FP16, each
 // section padded to a multiple of 16 bytes.
 #pragma once
@@ -27,26 +29,26 @@
 
 namespace mlpl {
 
-constexpr int kTileM = 16;  // output features per A fragment
-constexpr int kTileK = 32;  // input features per A fragment
+constexpr int kTileM = 32;  // output features per A fragment (and samples per B fragment)
+constexpr int kTileK = 16;  // input features per A fragment
 constexpr int kFragBytes = 64 * 8 * 2;
-constexpr int kBiasTileBytes = 16 * 4;
+constexpr int kBiasTileBytes = 32 * 4;
 
 constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 constexpr int k0_pad(int w0) { return round_up(w0, kTileK); }
 
 // w: the kernel's widths w[0..L]
 constexpr int m_tiles(const int *w, int l) { return (w[l + 1] + kTileM - 1) / kTileM; }
-constexpr int k_blocks(const int *w, int l)
-{
-    return l == 0 ? k0_pad(w[0]) / kTileK : (m_tiles(w, l - 1) + 1) / 2;
-}
+constexpr int k_blocks(const int *w, int l) { return (w[l] + kTileK - 1) / kTileK; }
 
 // Input feature carried by slot (kb, g, j) of layer l.
 constexpr int slot_feature(int l, int kb, int g, int j)
 {
-    return l == 0 ? kTileK * kb + 8 * g + j : 16 * (2 * kb + j / 4) + 4 * g + (j % 4);
+    return l == 0 ? kTileK * kb + 8 * g + j : kTileK * kb + 8 * (j / 4) + 4 * g + (j % 4);
 }
+
+// Output feature held in accumulator element j of lane group g for output tile mt.
+constexpr int acc_feature(int mt, int g, int j) { return kTileM * mt + 8 * (j / 4) + 4 * g + (j % 4); }
 
 constexpr size_t pk_a_bytes(const int *w, int l) { return (size_t)m_tiles(w, l) * k_blocks(w, l) * kFragBytes; }
 constexpr size_t pk_layer_bytes(const int *w, int l) { return pk_a_bytes(w, l) + (size_t)m_tiles(w, l) * kBiasTileBytes; }

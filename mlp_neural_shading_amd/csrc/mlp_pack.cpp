@@ -39,8 +39,8 @@ void pack_image(int n_layers, const int *widths, const int *kw, const uint16_t *
         for (int mt = 0; mt < MT; ++mt)
             for (int kb = 0; kb < KB; ++kb)
                 for (int lane = 0; lane < 64; ++lane) {
-                    const int g = lane / 16, m = lane % 16;
-                    const int r = 16 * mt + m;
+                    const int g = lane / 32, m = lane % 32;
+                    const int r = mlpl::kTileM * mt + m;
                     uint16_t *frag = A + ((size_t)(mt * KB + kb) * 64 + lane) * 8;
                     for (int j = 0; j < 8; ++j) {
                         const int f = mlpl::slot_feature(l, kb, g, j);
@@ -49,10 +49,10 @@ void pack_image(int n_layers, const int *widths, const int *kw, const uint16_t *
                 }
         float *B = (float *)(dst + mlpl::pk_b_off(kw, l));
         for (int mt = 0; mt < MT; ++mt)
-            for (int g = 0; g < 4; ++g)
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * mt + 4 * g + i;
-                    B[mt * 16 + g * 4 + i] = r < wout ? half_bits_to_float(b[r]) : 0.0f;
+            for (int g = 0; g < 2; ++g)
+                for (int j = 0; j < 16; ++j) {
+                    const int r = mlpl::acc_feature(mt, g, j);
+                    B[mt * 32 + g * 16 + j] = r < wout ? half_bits_to_float(b[r]) : 0.0f;
                 }
     }
 }

@@ -87,39 +87,45 @@ def test_pack_without_a_device_reports_hip_error():
 
 
 def test_plan_widths():
-    assert B.mlp_plan_widths(workloads.get("small").widths) == [32, 32, 32, 32, 32, 32, 32, 32, 16]
-    assert B.mlp_plan_widths(workloads.get("page").widths) == [32] + [64] * 7 + [16]
+    assert B.mlp_plan_widths(workloads.get("small").widths) == [16, 32, 32, 32, 32, 32, 32, 32, 32]
+    assert B.mlp_plan_widths(workloads.get("page").widths) == [32] + [64] * 7 + [32]
+    assert B.mlp_plan_widths(workloads.get("hetero").widths) == [32, 64, 64, 64, 128, 64, 64, 32, 32]
     assert B.mlp_plan_widths([2, 2, 1]) == [128, 128, 128]  # generic kernel, zero-padded
 
 
 # ---- an independent reading of the packed layout ---------------------------------------------
 #
-# Packed image, per layer: A fragments [mt][kb][lane][8] FP16 then bias tiles [mt][g][4] FP32, where
-# lane = 16 g + m holds row 16 mt + m; slot j of block kb holds input feature
-#   layer 0:  32 kb + 8 g + j
-#   layer >0: 16 (2 kb + j // 4) + 4 g + j % 4
-# and the bias tile entry (mt, g, i) is b[16 mt + 4 g + i].  Anything outside the real matrix is 0.
+# Packed image, per layer: A fragments [mt][kb][lane][8] FP16 then bias tiles [mt][g][16] FP32, where
+# lane = 32 g + m holds row 32 mt + m; slot j of block kb holds input feature
+#   layer 0:  16 kb + 8 g + j
+#   layer >0: 16 kb + 8 (j // 4) + 4 g + j % 4
+# and the bias tile entry (mt, g, j) is b[32 mt + 8 (j // 4) + 4 g + j % 4].  Anything outside the real
+# matrix is 0.  MT = ceil(w_out / 32) output tiles, KB = ceil(w_in / 16) input blocks.
 
 def _unpack(image, kw, widths):
     L = len(widths) - 1
     off = 0
     Ws, bs = [], []
     for l in range(L):
-        MT = -(-kw[l + 1] // 16)
-        KB = (-(-kw[0] // 32) * 32) // 32 if l == 0 else -(-(-(-kw[l] // 16)) // 2)
-        A = image[off:off + MT * KB * 1024].view(np.uint16).reshape(MT, KB, 4, 16, 8)
+        MT = -(-kw[l + 1] // 32)
+        KB = -(-kw[l] // 16)
+        A = image[off:off + MT * KB * 1024].view(np.uint16).reshape(MT, KB, 2, 32, 8)
         off += MT * KB * 1024
-        bias = image[off:off + MT * 64].view(np.float32).reshape(MT, 4, 4)
-        off += MT * 64
-        full = np.zeros((MT * 16, KB * 32), np.uint16)
+        bias = image[off:off + MT * 128].view(np.float32).reshape(MT, 2, 16)
+        off += MT * 128
+        full = np.zeros((MT * 32, KB * 16), np.uint16)
+        bfull = np.zeros(MT * 32, np.float32)
         for mt in range(MT):
+            for g in range(2):
+                for j in range(16):
+                    bfull[32 * mt + 8 * (j // 4) + 4 * g + j % 4] = bias[mt, g, j]
             for kb in range(KB):
-                for g in range(4):
+                for g in range(2):
                     for j in range(8):
-                        f = 32 * kb + 8 * g + j if l == 0 else 16 * (2 * kb + j // 4) + 4 * g + j % 4
-                        full[16 * mt:16 * mt + 16, f] = A[mt, kb, g, :, j]
+                        f = 16 * kb + 8 * g + j if l == 0 else 16 * kb + 8 * (j // 4) + 4 * g + j % 4
+                        full[32 * mt:32 * mt + 32, f] = A[mt, kb, g, :, j]
         Ws.append(full)
-        bs.append(bias.reshape(-1))
+        bs.append(bfull)
     assert off == image.size
     return Ws, bs
 
@@ -134,6 +140,7 @@ def test_packed_image_layout(name):
         Ws, bs = workloads.init_weights(widths)
     kw = B.mlp_plan_widths(widths)
     image = B.mlp_pack_host(Ws, bs, B.MLP_LAYOUT_PACKED)
+    assert image.size % 16 == 0
     assert image.size == B.mlp_packed_size(widths)
     UW, Ub = _unpack(image, kw, widths)
     for l in range(len(widths) - 1):
