@@ -72,6 +72,43 @@ def time_dispatches(torch, fn, n: int):
     return [a.elapsed_time(b) for a, b in ev]
 
 
+def measure_ceiling(torch):
+    """FP16 MFMA throughput the device sustains on random operands (v_mfma_f32_32x32x16_f16 loop,
+    4 waves per SIMD), alone and with 6 packed-FP16 VALU instructions per MFMA, and on all-zero
+    operands (which switch little and so let the clock stay high); see mlp_ceiling.h."""
+    import ctypes
+
+    lib = ctypes.CDLL(str(ROOT / "mlp_neural_shading_amd" / "libmlp_ceiling.so"))
+    lib.mlp_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_void_p]
+    props = torch.cuda.get_device_properties(0)
+    grid = props.multi_processor_count * 4
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    random_ops = (torch.rand(16384, device="cuda", generator=gen) * 2 - 1).to(torch.float16)
+    zero_ops = torch.zeros(16384, dtype=torch.float16, device="cuda")
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, operands, k in (("valu_per_mfma_0", random_ops, 0), ("valu_per_mfma_6", random_ops, 6),
+                              ("zero_operands", zero_ops, 0)):
+        iters = 20000
+
+        def run():
+            rc = lib.mlp_ceiling_launch(k, grid, operands.data_ptr(), out.data_ptr(), clk.data_ptr(), iters,
+                                        stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("ceiling probe launch failed (%d)" % rc)
+
+        run()
+        ms = statistics.median(time_dispatches(torch, run, 3))
+        cyc, ticks = clk.cpu().tolist()
+        flops = grid * 4 * iters * 8 * 32768
+        res[name] = {"tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "clock_mhz": round(cyc / (ticks / 100.0)) if ticks else None}
+    return res
+
+
 def cpu_baseline(wl, Ws, bs, x_dev, rows: int):
     import numpy as np
     import torch
@@ -98,7 +135,22 @@ def main() -> int:
     ap.add_argument("--workload", default="page", help="workload name or alias (default: page)")
     ap.add_argument("--no-variants", action="store_true", help="skip the row-major / scalarised A/B")
     ap.add_argument("--cpu-rows", type=int, default=16384, help="rows of the CPU-oracle sample (0: skip)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the random-operand MFMA ceiling probe")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy five times (scales HBM counters)")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+
+        src = torch.randn(64 * 1024 * 1024, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read_per_launch": src.numel() * 4,
+                          "copy_probe_bytes_written_per_launch": src.numel() * 4}))
+        return 0
 
     if args.gpus != 1:
         print("bench.py measures one GPU: the workload's rows are independent, so N GPUs would each run "
@@ -171,6 +223,12 @@ def main() -> int:
                     "frac_fp16_peak": round(flops_per_launch / (med * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
                     "kernel": B.mlp_kernel_name(act)}
         B.mlp_pack_weights(Ws, bs, B.MLP_LAYOUT_PACKED, sh)
+
+    if not args.no_ceiling:
+        ceiling = measure_ceiling(torch)
+        roofline["measured_ceiling"] = dict(ceiling, kind="v_mfma_f32_32x32x16_f16 loop on random FP16 operands")
+        c = ceiling["valu_per_mfma_0"]["tflops"]
+        roofline["frac_of_measured_ceiling"] = round(achieved_tflops / c, 4)
 
     cpu = None
     if args.cpu_rows > 0:

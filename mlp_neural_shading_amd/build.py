@@ -27,6 +27,8 @@ COMMON = [
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 SOURCES = ["mlp_kernels.hip", "mlp_api.cpp", "mlp_pack.cpp"]
+CEILING_SOURCE = "mlp_ceiling.hip"
+CEILING_LIB = PKG / "libmlp_ceiling.so"
 
 
 INCLUDE = PKG.parent / "include"
@@ -51,8 +53,17 @@ def build(verbose: bool = False, extra=()) -> Path:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr[-8000:]))
     os.replace(tmp, LIB)
+    # the benchmark's MFMA-ceiling probe, a separate small library
+    cobj = BUILD_DIR / "mlp_ceiling.o"
+    _compile(CSRC / CEILING_SOURCE, cobj, list(extra))
+    tmp = CEILING_LIB.with_name(CEILING_LIB.name + ".tmp%d" % os.getpid())
+    r = subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", str(cobj), "-o", str(tmp)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed for the ceiling probe:\n%s" % r.stderr[-8000:])
+    os.replace(tmp, CEILING_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", CEILING_LIB)
     return LIB
 
 
