@@ -9,9 +9,15 @@ inference", section "Experiment setup").  Prints one JSON line:
   value        M evals/s over exactly --steps steps (wall clock, synchronised on both sides)
   roofline     algorithmic FLOPs per launch / mean launch time (HIP events on the launch stream)
                against the FP16 dense MFMA peak; traffic from committed rocprofv3 counters
-  variants     the page's two A/B comparisons: row-major vs packed weights, scalarised vs vector
-               activation (per-dispatch event medians, interleaved per layout)
-  cpu_baseline the CPU oracle on a bounded sample of the same rows, one host thread
+  variants     the page's two A/B comparisons, row-major vs packed weights and scalarised vs vector
+               activation: 3 processes, each timing 3 warm-ups + 10 dispatches per variant with HIP
+               events (variants interleaved), reported as the median of the 3 process medians with
+               min and max
+  workloads    every workload (all five network shapes) timed the same way, with the FP16 MFMA and
+               the HBM fraction of each
+  dispatch     an empty kernel timed the same way, and the wall-clock gap between back-to-back steps
+  clocks       the GPU clocks reported by rocm-smi before and after the measurements
+  cpu_baseline the CPU oracle on a bounded sample of the same rows, one host thread pinned to a core
 """
 from __future__ import annotations
 
@@ -72,15 +78,137 @@ def time_dispatches(torch, fn, n: int):
     return [a.elapsed_time(b) for a, b in ev]
 
 
-def measure_ceiling(torch):
-    """FP16 MFMA throughput the device sustains on random operands (v_mfma_f32_32x32x16_f16 loop,
-    4 waves per SIMD), alone and with 6 packed-FP16 VALU instructions per MFMA, and on all-zero
-    operands (which switch little and so let the clock stay high); see mlp_ceiling.h."""
+def ceiling_lib():
     import ctypes
 
     lib = ctypes.CDLL(str(ROOT / "mlp_neural_shading_amd" / "libmlp_ceiling.so"))
     lib.mlp_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_int, ctypes.c_void_p]
+    lib.mlp_ceiling_empty_launch.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
+def roofline_grid(B, wl) -> int:
+    """Workgroups of the inference kernel for this workload (one per compute unit when persistent)."""
+    import torch
+
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def measure_empty_dispatch(torch, grid: int) -> float:
+    """Median event-timed duration (ms) of an empty kernel with the inference kernel's grid size."""
+    lib = ceiling_lib()
+    stream = torch.cuda.current_stream()
+
+    def run():
+        if lib.mlp_ceiling_empty_launch(grid, stream.cuda_stream) != 0:
+            raise RuntimeError("empty-kernel launch failed")
+
+    for _ in range(3):
+        run()
+    return statistics.median(time_dispatches(torch, run, 10))
+
+
+def variant_medians(torch, B, wl, Ws, bs, x, y, order=(0, 1)) -> dict:
+    """One process's share of the A/B protocol: per layout (in `order`), pack, then for the vector and
+    the scalarised activation in turn 3 warm-up dispatches and 10 event-timed ones; returns the median
+    (ms) of each variant's 10."""
+    sh = torch.cuda.current_stream().cuda_stream
+    names = {B.MLP_LAYOUT_PACKED: "packed", B.MLP_LAYOUT_ROW_MAJOR: "rowmajor"}
+    layouts = [B.MLP_LAYOUT_PACKED, B.MLP_LAYOUT_ROW_MAJOR]
+    out = {}
+    for i in order:
+        layout = layouts[i]
+        B.mlp_pack_weights(Ws, bs, layout, sh)
+        for act, aname in ((B.MLP_ACT_VECTOR, "vector"), (B.MLP_ACT_SCALARISED, "scalarised")):
+            f = lambda a=act: B.mlp_infer_ex(wl.batch, x.data_ptr(), y.data_ptr(), sh, a)
+            for _ in range(3):
+                f()
+            out["%s+%s" % (names[layout], aname)] = {"ms": statistics.median(time_dispatches(torch, f, 10)),
+                                                      "kernel": B.mlp_kernel_name(act)}
+    B.mlp_pack_weights(Ws, bs, B.MLP_LAYOUT_PACKED, sh)
+    return out
+
+
+def summarise_variants(runs, wl) -> dict:
+    """Median of the per-process medians, with min and max, for each variant."""
+    flops = wl.flops_per_eval * wl.batch
+    res = {}
+    for name in runs[0]:
+        ms = [r[name]["ms"] for r in runs]
+        med = statistics.median(ms)
+        res[name] = {"median_of_medians_ms": round(med, 6), "min_ms": round(min(ms), 6), "max_ms": round(max(ms), 6),
+                     "processes": len(ms), "m_evals_per_s": round(throughput_m_evals(wl.batch, med), 1),
+                     "frac_fp16_peak": round(flops / (med * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
+                     "kernel": runs[0][name]["kernel"]}
+    return res
+
+
+def protocol_variants(wl_name: str, processes: int = 3) -> list:
+    """Run the A/B protocol in `processes` fresh processes, one after another (alternating which
+    layout goes first); returns each process's medians."""
+    import subprocess
+
+    runs = []
+    for i in range(processes):
+        cmd = [sys.executable, str(Path(__file__).resolve()), "--protocol-child", "--workload", wl_name,
+               "--layout-order", "01" if i % 2 == 0 else "10"]
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        if r.returncode != 0:
+            raise RuntimeError("A/B child process failed (%d): %s" % (r.returncode, r.stderr[-2000:]))
+        runs.append(json.loads(r.stdout.strip().splitlines()[-1]))
+    return runs
+
+
+def measure_workloads(torch, B, workloads, skip: str) -> dict:
+    """Every workload with the packed image: median of 20 event-timed dispatches (after 3 warm-ups),
+    its M evals/s, its fraction of the FP16 MFMA peak and of the HBM peak, and the four variants
+    (3 interleaved rounds in this process, median of the round medians)."""
+    res = {}
+    dev = torch.device("cuda:0")
+    sh = torch.cuda.current_stream().cuda_stream
+    for name, wl in workloads.WORKLOADS.items():
+        Ws, bs = wl.weights()
+        x = wl.inputs(device=dev)
+        y = torch.empty((wl.batch, wl.widths[-1]), dtype=torch.float16, device=dev)
+        B.mlp_pack_weights(Ws, bs, B.MLP_LAYOUT_PACKED, sh)
+        f = lambda: B.mlp_infer(wl.batch, x.data_ptr(), y.data_ptr(), sh)
+        for _ in range(3):
+            f()
+        ms = statistics.median(time_dispatches(torch, f, 20))
+        tflops = wl.flops_per_eval * wl.batch / (ms * 1e-3) / 1e12
+        gbs = wl.io_bytes_per_eval * wl.batch / (ms * 1e-3) / 1e9
+        entry = {"widths": list(wl.widths), "batch": wl.batch, "median_ms": round(ms, 6),
+                 "m_evals_per_s": round(throughput_m_evals(wl.batch, ms), 1), "tflops": round(tflops, 1),
+                 "frac_fp16_peak": round(tflops / PEAK_FP16_TFLOPS, 4), "io_gbs": round(gbs, 1),
+                 "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "kernel": B.mlp_kernel_name(B.MLP_ACT_VECTOR)}
+        if name != skip:
+            rounds = [variant_medians(torch, B, wl, Ws, bs, x, y, (0, 1) if r % 2 == 0 else (1, 0)) for r in range(3)]
+            entry["variants"] = summarise_variants(rounds, wl)
+        res[name] = entry
+        del x, y
+        torch.cuda.empty_cache()
+    return res
+
+
+def read_clocks() -> dict:
+    """Current SCLK / MCLK as rocm-smi reports them (best effort; the clocks cannot be locked here)."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+        card = next(iter(data.values()))
+        return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()}
+    except Exception as e:  # the tool may be missing or print something else
+        return {"error": "%s: %s" % (type(e).__name__, str(e)[:200])}
+
+
+def measure_ceiling(torch):
+    """FP16 MFMA throughput the device sustains on random operands (v_mfma_f32_32x32x16_f16 loop,
+    4 waves per SIMD), alone and with 6 packed-FP16 VALU instructions per MFMA, and on all-zero
+    operands (which switch little and so let the clock stay high); see mlp_ceiling.h."""
+    lib = ceiling_lib()
     props = torch.cuda.get_device_properties(0)
     grid = props.multi_processor_count * 4
     gen = torch.Generator(device="cuda").manual_seed(1)
@@ -109,7 +237,18 @@ def measure_ceiling(torch):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(wl, Ws, bs, x_dev, rows: int):
+    """The C oracle, single-threaded and pinned to one core, on the first `rows` rows."""
     import numpy as np
     import torch
 
@@ -118,13 +257,21 @@ def cpu_baseline(wl, Ws, bs, x_dev, rows: int):
     xb = x_dev[:rows].cpu().view(torch.int16).numpy().view(np.uint16)
     o = oracle.default()
     o.mlp_forward(Ws, bs, xb[:64])  # load and warm the library
-    t0 = time.perf_counter()
-    o.mlp_forward(Ws, bs, xb, threads=1)
-    dt = time.perf_counter() - t0
+    allowed = os.sched_getaffinity(0)
+    core = max(allowed)
+    os.sched_setaffinity(0, {core})  # this thread only
+    try:
+        t0 = time.perf_counter()
+        o.mlp_forward(Ws, bs, xb, threads=1)
+        dt = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, allowed)
     return {"value": round(throughput_m_evals(rows, dt * 1e3), 6), "unit": "M evals/s", "cores": 1,
             "kind": "oracle",
-            "sample": "first %d of the %d rows, single-threaded C oracle (gcc -O2), %.1f s on %s"
-                      % (rows, wl.batch, dt, platform.processor() or platform.machine())}
+            "sample": "first %d of the %d rows (all %d distinct inputs), single-threaded C oracle (gcc %s) pinned "
+                      "to CPU %d of %d visible, %.1f s on %s"
+                      % (rows, wl.batch, wl.unique_rows, " ".join(oracle.CFLAGS[:4]), core, len(allowed), dt,
+                         cpu_model())}
 
 
 def main() -> int:
@@ -134,7 +281,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="page", help="workload name or alias (default: page)")
     ap.add_argument("--no-variants", action="store_true", help="skip the row-major / scalarised A/B")
-    ap.add_argument("--cpu-rows", type=int, default=16384, help="rows of the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=65536, help="rows of the CPU-oracle sample (0: skip)")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--protocol-child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--layout-order", default="01", help=argparse.SUPPRESS)
     ap.add_argument("--no-ceiling", action="store_true", help="skip the random-operand MFMA ceiling probe")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy five times (scales HBM counters)")
@@ -152,6 +302,20 @@ def main() -> int:
                           "copy_probe_bytes_written_per_launch": src.numel() * 4}))
         return 0
 
+    if args.protocol_child:
+        import torch
+
+        from mlp_neural_shading_amd import binding as B
+        from mlp_neural_shading_amd import workloads
+
+        wl = workloads.get(args.workload)
+        Ws, bs = wl.weights()
+        x = wl.inputs(device="cuda:0")
+        y = torch.empty((wl.batch, wl.widths[-1]), dtype=torch.float16, device="cuda:0")
+        order = tuple(int(c) for c in args.layout_order)
+        print(json.dumps(variant_medians(torch, B, wl, Ws, bs, x, y, order)), flush=True)
+        return 0
+
     if args.gpus != 1:
         print("bench.py measures one GPU: the workload's rows are independent, so N GPUs would each run "
               "the same kernel on 1/N of the rows; only --gpus 1 is supported.", file=sys.stderr)
@@ -165,6 +329,7 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    clocks_before = read_clocks()
     wl = workloads.get(args.workload)
     Ws, bs = wl.weights()
     x = wl.inputs(device=dev)
@@ -204,31 +369,24 @@ def main() -> int:
                 "median_launch_ms": round(statistics.median(launch_ms), 6),
                 "io_gbs": round(wl.io_bytes_per_eval * wl.batch / (mean_launch_ms * 1e-3) / 1e9, 1)}
 
+    dispatch = {"empty_kernel_ms": round(measure_empty_dispatch(torch, roofline_grid(B, wl)), 6),
+                "step_minus_kernel_ms": round(ms_per_step - mean_launch_ms, 6)}
+
     variants = {}
     if not args.no_variants:
-        for layout, lname in ((B.MLP_LAYOUT_PACKED, "packed"), (B.MLP_LAYOUT_ROW_MAJOR, "rowmajor")):
-            B.mlp_pack_weights(Ws, bs, layout, sh)
-            times = {0: [], 1: []}
-            for rnd in range(3):  # interleave the two activation forms, A B A B A B
-                for act in (B.MLP_ACT_VECTOR, B.MLP_ACT_SCALARISED):
-                    f = lambda a=act: B.mlp_infer_ex(wl.batch, x.data_ptr(), y.data_ptr(), sh, a)
-                    for _ in range(3):
-                        f()
-                    times[act].append(statistics.median(time_dispatches(torch, f, 10)))
-            for act, aname in ((B.MLP_ACT_VECTOR, "vector"), (B.MLP_ACT_SCALARISED, "scalarised")):
-                med = statistics.median(times[act])
-                variants["%s+%s" % (lname, aname)] = {
-                    "median_of_medians_ms": round(med, 6),
-                    "m_evals_per_s": round(throughput_m_evals(wl.batch, med), 1),
-                    "frac_fp16_peak": round(flops_per_launch / (med * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
-                    "kernel": B.mlp_kernel_name(act)}
-        B.mlp_pack_weights(Ws, bs, B.MLP_LAYOUT_PACKED, sh)
+        variants = summarise_variants(protocol_variants(wl.name), wl)
 
     if not args.no_ceiling:
         ceiling = measure_ceiling(torch)
         roofline["measured_ceiling"] = dict(ceiling, kind="v_mfma_f32_32x32x16_f16 loop on random FP16 operands")
         c = ceiling["valu_per_mfma_0"]["tflops"]
         roofline["frac_of_measured_ceiling"] = round(achieved_tflops / c, 4)
+
+    per_workload = {}
+    if not args.no_workloads:
+        per_workload = measure_workloads(torch, B, workloads, skip=wl.name)
+        per_workload[wl.name]["variants"] = variants
+    clocks_after = read_clocks()
 
     cpu = None
     if args.cpu_rows > 0:
@@ -254,6 +412,11 @@ def main() -> int:
         "pack_ms": round(pack_ms, 4),
         "roofline": roofline,
         "variants": variants,
+        "dispatch": dispatch,
+        "workloads": per_workload,
+        "clocks": {"before": clocks_before, "after": clocks_after,
+                   "note": "clocks are not locked on this machine; the kernel-side clock of the ceiling probe "
+                           "is in roofline.measured_ceiling"},
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
     }

@@ -24,6 +24,11 @@ extern "C" {
 int mlp_ceiling_launch(int valu_per_mfma, int grid, const void *operands, float *out, uint64_t *clk, int iters,
                        void *stream);
 
+/* Enqueue one launch of an empty kernel (`grid` workgroups of 64 threads that do nothing) on `stream`:
+ * the fixed cost of one dispatch, timed the same way as the inference kernel.
+ * Returns 0, -1 if grid < 1, -5 if the launch failed. */
+int mlp_ceiling_empty_launch(int grid, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,6 +55,8 @@ __global__ __launch_bounds__(256) void mfma_loop(const h8 *src, float *out, uint
     }
 }
 
+__global__ __launch_bounds__(64) void empty_kernel() {}
+
 }  // namespace
 
 extern "C" int mlp_ceiling_launch(int valu_per_mfma, int grid, const void *operands, float *out, uint64_t *clk,
@@ -67,5 +69,13 @@ extern "C" int mlp_ceiling_launch(int valu_per_mfma, int grid, const void *opera
     case 6: hipLaunchKernelGGL(mfma_loop<6>, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const h8 *)operands, out, clk, iters); break;
     default: return -1;
     }
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int mlp_ceiling_empty_launch(int grid, void *stream)
+{
+    if (grid < 1)
+        return -1;
+    hipLaunchKernelGGL(empty_kernel, dim3(grid), dim3(64), 0, (hipStream_t)stream);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }

@@ -1,0 +1,36 @@
+"""Host-side checks of the benchmark and its probe library (no GPU needed): the probe library exports
+what include/mlp_ceiling.h declares, the benchmark refuses more than one GPU with a message, and the
+throughput arithmetic is right."""
+import re
+import subprocess
+import sys
+from pathlib import Path
+
+import bench
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+def test_ceiling_library_exports_declared_functions():
+    import ctypes
+
+    decls = set(re.findall(r"^\s*int\s+(mlp_ceiling\w+)\s*\(", (ROOT / "include" / "mlp_ceiling.h").read_text(), re.M))
+    assert decls == {"mlp_ceiling_launch", "mlp_ceiling_empty_launch"}
+    lib = ctypes.CDLL(str(ROOT / "mlp_neural_shading_amd" / "libmlp_ceiling.so"))
+    for name in decls:
+        assert hasattr(lib, name), name
+    # argument checks happen before any HIP call
+    lib.mlp_ceiling_empty_launch.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    assert lib.mlp_ceiling_empty_launch(0, None) == -1
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_throughput_arithmetic():
+    # 1,048,576 evaluations in 0.0524288 ms = 20,000 M evals/s
+    assert abs(bench.throughput_m_evals(1 << 20, 0.0524288) - 20000.0) < 1e-6
