@@ -17,8 +17,9 @@
 //     where the next layer's B operand needs it, so activations never leave the registers;
 //   - the last layer converts to FP16 (no activation) and stores the row's outputs.
 // Variants for the page's two A/B comparisons: the row-major weight image (fragments assembled from
-// the canonical [out][in] matrices with per-lane index arithmetic), and the scalarised activation
-// (one component at a time, compare and branch, "if (v < 0) v *= half(0.01)").
+// the canonical [out][in] matrices with per-lane index arithmetic; staged in LDS with padded rows),
+// and the scalarised activation (one component at a time, compare and branch,
+// "if (v < 0) v *= half(0.01)").
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -94,6 +95,8 @@ struct Net {
     static constexpr int MT(int l) { return mlpl::m_tiles(w, l); }
     static constexpr int KB(int l) { return mlpl::k_blocks(w, l); }
     static constexpr size_t image_bytes(int layout) { return layout == kPacked ? mlpl::pk_bytes(w, L) : mlpl::rm_bytes(w, L); }
+    // Bytes of the image as staged in LDS (row-major rows are padded there).
+    static constexpr size_t lds_bytes(int layout) { return layout == kPacked ? mlpl::pk_bytes(w, L) : mlpl::rml_bytes(w, L); }
 };
 
 template <class N, int NT, int LAYOUT, int ACT, bool GENERIC, bool LDS_W, class Src>
@@ -112,24 +115,26 @@ struct Body {
         if constexpr (LAYOUT == kPacked) {
             return src.load16(lane * 16, (int)mlpl::pk_a_off(N::w, l) + (mt * KB + kb) * mlpl::kFragBytes);
         } else {
-            // Row-major [out][in]: lane (g, m) gathers row 32 mt + m at its slot features.
+            // Row-major [out][in]: lane (g, m) gathers row 32 mt + m at its slot features.  In LDS
+            // the rows are padded (mlp_layout.h), in global memory they are as given.
             constexpr int win = N::w[l], wout = N::w[l + 1];
-            static_assert(l > 0 || win % 8 == 0, "row-major input layer needs w0 % 8 == 0");
-            static_assert(l == 0 || win % 4 == 0, "row-major hidden layer needs w % 4 == 0");
+            static_assert(win % 8 == 0, "row-major layers need w_in % 8 == 0");
+            constexpr int stride = LDS_W ? mlpl::rml_stride(win) : win * 2;
+            constexpr int w_off = LDS_W ? (int)mlpl::rml_w_off(N::w, l) : (int)mlpl::rm_w_off(N::w, l);
             const int g = lane >> 5, m = lane & 31;
             const int r = 32 * mt + m;
-            const int row = (int)mlpl::rm_w_off(N::w, l) + 32 * mt * win * 2;  // wave-uniform
+            const int row = w_off + 32 * mt * stride;  // wave-uniform
             h8 a = (h8)(_Float16)0;
             if constexpr (l == 0) {
                 if (r < wout && 16 * kb + 8 * g < win)
-                    a = src.load16((m * win + 8 * g) * 2, row + 16 * kb * 2);
+                    a = src.load16(m * stride + 8 * g * 2, row + 16 * kb * 2);
             } else {
                 const int f0 = 16 * kb + 4 * g, f1 = f0 + 8;
                 h4 lo = (h4)(_Float16)0, hi = (h4)(_Float16)0;
                 if (r < wout && f0 < win)
-                    lo = src.load8((m * win + 4 * g) * 2, row + 16 * kb * 2);
+                    lo = src.load8(m * stride + 4 * g * 2, row + 16 * kb * 2);
                 if (r < wout && f1 < win)
-                    hi = src.load8((m * win + 4 * g) * 2, row + (16 * kb + 8) * 2);
+                    hi = src.load8(m * stride + 4 * g * 2, row + (16 * kb + 8) * 2);
                 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
             return a;
@@ -152,7 +157,7 @@ struct Body {
         } else {
             constexpr int wout = N::w[l + 1];
             static_assert(wout % 4 == 0, "row-major layer needs w_out % 4 == 0");
-            const int soff = (int)mlpl::rm_b_off(N::w, l) + 32 * mt * 2;
+            const int soff = (LDS_W ? (int)mlpl::rml_b_off(N::w, l) : (int)mlpl::rm_b_off(N::w, l)) + 32 * mt * 2;
             h4 q[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -397,6 +402,36 @@ __device__ __forceinline__ void stage_image(uint8_t *lds, const uint8_t *image, 
     ((K * THREADS * 16 + t16 < BYTES ? (void)(*(uint4 *)(lds + K * THREADS * 16 + t16) = v[K]) : (void)0), ...);
 }
 
+// LDS offset of the 16-byte chunk at byte offset g of a row-major image (all widths multiples of 8,
+// so every row is a whole number of chunks): its row moves to the padded row stride.
+template <class N, int... L>
+__device__ __forceinline__ int rowmajor_lds_offset(int g, std::integer_sequence<int, L...>)
+{
+    int o = 0;
+    const auto one = [&](auto lc) {
+        constexpr int l = decltype(lc)::value;
+        constexpr int w0 = (int)mlpl::rm_w_off(N::w, l), b0 = (int)mlpl::rm_b_off(N::w, l);
+        constexpr int end = (int)mlpl::rm_w_off(N::w, l + 1), row = N::w[l] * 2;
+        if (g >= w0 && g < end)
+            o = g < b0 ? (int)mlpl::rml_w_off(N::w, l) + (g - w0) / row * mlpl::rml_stride(N::w[l]) + (g - w0) % row
+                       : (int)mlpl::rml_b_off(N::w, l) + (g - b0);
+    };
+    (one(std::integral_constant<int, L>()), ...);
+    return o;
+}
+
+// Stage a row-major image into LDS with padded rows (same load pattern as stage_image).
+template <class N, int BYTES, int THREADS, int... K>
+__device__ __forceinline__ void stage_rowmajor(uint8_t *lds, const uint8_t *image, std::integer_sequence<int, K...>)
+{
+    const int t16 = (int)threadIdx.x * 16;
+    const uint4 v[] = {*(const uint4 *)(image + (K * THREADS * 16 + t16 < BYTES ? K * THREADS * 16 + t16 : BYTES - 16))...};
+    ((K * THREADS * 16 + t16 < BYTES
+          ? (void)(*(uint4 *)(lds + rowmajor_lds_offset<N>(K * THREADS * 16 + t16, std::make_integer_sequence<int, N::L>())) = v[K])
+          : (void)0),
+     ...);
+}
+
 // EU: waves per SIMD the instance is built for (its register budget is 512 / EU per lane).
 //
 // Work distribution: workgroup b owns the contiguous tiles [lo, hi) of an even split; its waves take
@@ -410,6 +445,7 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
     using Src = typename std::conditional<LDS_W, LdsSource, BufferSource>::type;
     using B = Body<N, NT, LAYOUT, ACT, GENERIC, LDS_W, Src>;
     constexpr int bytes = (int)N::image_bytes(LAYOUT);
+    constexpr int lbytes = (int)N::lds_bytes(LAYOUT);
     static_assert(bytes % 16 == 0, "image must be a multiple of 16 bytes");
     constexpr int kRows = NT * 32;
     __shared__ int next_tile;
@@ -431,9 +467,12 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
 
     Src src;
     if constexpr (LDS_W) {
-        __shared__ __attribute__((aligned(16))) uint8_t lds[bytes];
+        __shared__ __attribute__((aligned(16))) uint8_t lds[lbytes];
         constexpr int kChunks = (bytes + WAVES * 64 * 16 - 1) / (WAVES * 64 * 16);
-        stage_image<bytes, WAVES * 64>(lds, a.image, std::make_integer_sequence<int, kChunks>());
+        if constexpr (LAYOUT == kPacked)
+            stage_image<bytes, WAVES * 64>(lds, a.image, std::make_integer_sequence<int, kChunks>());
+        else
+            stage_rowmajor<N, bytes, WAVES * 64>(lds, a.image, std::make_integer_sequence<int, kChunks>());
         src.base = lds;
     } else {
         src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.image, 0, bytes, kBufferRsrcWord3);

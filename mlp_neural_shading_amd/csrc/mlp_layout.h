@@ -74,4 +74,21 @@ constexpr size_t rm_w_off(const int *w, int l)
 constexpr size_t rm_b_off(const int *w, int l) { return rm_w_off(w, l) + rm_w_bytes(w, l); }
 constexpr size_t rm_bytes(const int *w, int L) { return rm_w_off(w, L); }
 
+// Row-major image as staged in LDS: the same matrices, each row padded by 16 bytes.  A fragment read
+// touches 16 consecutive rows at once; with a row stride of w_in * 2 + 16 bytes (w_in a multiple of
+// 8) the rows start 4 (mod 64) banks apart, so the 16 rows fall in distinct groups of four banks
+// ("Optimization Techniques", "Avoiding Bank Conflicts": pad the row stride).  Unpadded, a 64-wide
+// layer's 128-byte rows all start in the same bank.
+constexpr int rml_stride(int win) { return win * 2 + 16; }
+constexpr size_t rml_w_bytes(const int *w, int l) { return (size_t)w[l + 1] * rml_stride(w[l]); }
+constexpr size_t rml_w_off(const int *w, int l)
+{
+    size_t o = 0;
+    for (int i = 0; i < l; ++i)
+        o += rml_w_bytes(w, i) + rm_b_bytes(w, i);
+    return o;
+}
+constexpr size_t rml_b_off(const int *w, int l) { return rml_w_off(w, l) + rml_w_bytes(w, l); }
+constexpr size_t rml_bytes(const int *w, int L) { return rml_w_off(w, L); }
+
 }  // namespace mlpl
