@@ -88,6 +88,22 @@ int mlp_pack_host(int n_layers, const int32_t *widths, const uint16_t *const *we
 int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const *weights,
                      const uint16_t *const *biases, int layout, void *stream);
 
+/* The same one-time conversion from weights already resident on the device, run as a kernel on
+ * `stream` ("Row-major versus InferencingOptimal weights": the conversion can be recorded into the
+ * GPU's command stream instead of run on the host).  The resulting device image is bit for bit the
+ * one mlp_pack_weights builds, and it becomes the current network.
+ *   d_weights n_layers host-memory entries, each a device pointer to [widths[l+1]][widths[l]] FP16
+ *             row-major, 2-byte aligned
+ *   d_biases  n_layers host-memory entries, each a device pointer to [widths[l+1]] FP16
+ *   stream    hipStream_t (NULL = the default stream) the conversion is enqueued on
+ * Stream-ordered: the call allocates the image, enqueues the conversion and returns without waiting.
+ * The weights must stay valid, and unchanged, until the stream has run the conversion; an
+ * mlp_infer on the same stream sees the converted image, one on another stream must first wait for
+ * this stream (e.g. with an event).  Ownership, threading and errors as for mlp_pack_weights, except
+ * that a device-side fault surfaces at the caller's next synchronisation. */
+int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *const *d_weights,
+                            const void *const *d_biases, int layout, void *stream);
+
 /* Evaluate the current network on `batch` rows: enqueue one kernel on `stream` and return.
  *   batch    number of rows, >= 0 (0: nothing is launched, returns MLP_OK)
  *   in_ptr   device pointer, [batch][widths[0]] FP16 row-major, 16-byte aligned

@@ -30,7 +30,8 @@ MLP_MAX_LAYERS = 8
 MLP_MAX_WIDTH = 128
 
 EXPORTED = (
-    "mlp_packed_size", "mlp_plan_widths", "mlp_pack_host", "mlp_pack_weights", "mlp_infer",
+    "mlp_packed_size", "mlp_plan_widths", "mlp_pack_host", "mlp_pack_weights", "mlp_pack_weights_device",
+    "mlp_infer",
     "mlp_infer_ex", "mlp_set_activation_mode", "mlp_kernel_name", "mlp_debug_read_packed",
     "mlp_last_error", "mlp_release",
 )
@@ -57,6 +58,7 @@ def lib() -> ctypes.CDLL:
             "mlp_plan_widths": ([i32, p, i32, p], i32),
             "mlp_pack_host": ([i32, p, p, p, i32, p, sz], i32),
             "mlp_pack_weights": ([i32, p, p, p, i32, p], i32),
+            "mlp_pack_weights_device": ([i32, p, p, p, i32, p], i32),
             "mlp_infer": ([i64, p, p, p], i32),
             "mlp_infer_ex": ([i64, p, p, p, i32], i32),
             "mlp_set_activation_mode": ([i32], i32),
@@ -142,6 +144,18 @@ def mlp_pack_weights(weights, biases, layout: int = MLP_LAYOUT_PACKED, stream=No
     w = _widths(ws.widths if widths is None else widths)
     _check(lib().mlp_pack_weights(len(w) - 1, w.ctypes.data, ws.wp, ws.bp, layout, _stream(stream)),
            "mlp_pack_weights")
+
+
+def mlp_pack_weights_device(weight_ptrs, bias_ptrs, widths, layout: int = MLP_LAYOUT_PACKED, stream=None) -> None:
+    """weight_ptrs / bias_ptrs: device addresses (ints, e.g. tensor.data_ptr()) of each layer's FP16
+    [out][in] matrix and [out] bias; widths: the n_layers + 1 widths."""
+    w = _widths(widths)
+    n = len(w) - 1
+    wp = (ctypes.c_void_p * max(n, 1))(*[int(a) for a in weight_ptrs])
+    bp = (ctypes.c_void_p * max(n, 1))(*[int(a) for a in bias_ptrs])
+    _check(lib().mlp_pack_weights_device(n, w.ctypes.data, wp if len(weight_ptrs) else None,
+                                         bp if len(bias_ptrs) else None, layout, _stream(stream)),
+           "mlp_pack_weights_device")
 
 
 def mlp_infer(batch: int, in_ptr: int, out_ptr: int, stream=None) -> None:

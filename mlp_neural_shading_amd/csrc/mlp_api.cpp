@@ -181,17 +181,13 @@ int mlp_pack_host(int n_layers, const int32_t *widths, const uint16_t *const *we
     return ok();
 }
 
-int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const *weights,
-                     const uint16_t *const *biases, int layout, void *stream)
-{
-    const KernelEntry *e = nullptr;
-    int rc = plan(n_layers, widths, layout, &e);
-    if (rc == MLP_OK)
-        rc = check_weights(n_layers, weights, biases);
-    if (rc != MLP_OK)
-        return rc;
+}  // extern "C"
 
-    State next;
+namespace {
+
+// A new State for (shape, layout) served by `e`, with its device image allocated (contents unset).
+int new_state(int n_layers, const int32_t *widths, int layout, const KernelEntry *e, State &next)
+{
     next.n_layers = n_layers;
     for (int i = 0; i <= n_layers; ++i)
         next.widths[i] = widths[i];
@@ -199,9 +195,6 @@ int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const 
     next.entry[MLP_ACT_VECTOR] = e;
     next.entry[MLP_ACT_SCALARISED] = select(n_layers, widths, layout, MLP_ACT_SCALARISED);
     next.bytes = mlpk::image_bytes(n_layers, e->widths, layout);
-    std::vector<uint8_t> host(next.bytes);
-    mlpk::pack_image(n_layers, widths, e->widths, weights, biases, layout, host.data());
-
     hipError_t err = hipGetDevice(&next.device);
     if (err != hipSuccess)
         return hip_fail(err, "hipGetDevice");
@@ -223,20 +216,82 @@ int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const 
     }
     err = hipMalloc(&next.image, next.bytes);
     if (err != hipSuccess) {
+        next.image = nullptr;
         const int code = err == hipErrorOutOfMemory ? MLP_ERR_OUT_OF_MEMORY : MLP_ERR_HIP;
         return fail(code, "hipMalloc(%zu) failed: %s", next.bytes, hipGetErrorString(err));
     }
-    err = hipMemcpyAsync(next.image, host.data(), next.bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
+    return MLP_OK;
+}
+
+void commit_state(State &next)
+{
+    next.packed = true;
+    if (g_net.packed)
+        (void)hipFree(g_net.image);
+    g_net = next;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const *weights,
+                     const uint16_t *const *biases, int layout, void *stream)
+{
+    const KernelEntry *e = nullptr;
+    int rc = plan(n_layers, widths, layout, &e);
+    if (rc == MLP_OK)
+        rc = check_weights(n_layers, weights, biases);
+    if (rc != MLP_OK)
+        return rc;
+    std::vector<uint8_t> host(mlpk::image_bytes(n_layers, e->widths, layout));
+    mlpk::pack_image(n_layers, widths, e->widths, weights, biases, layout, host.data());
+
+    State next;
+    rc = new_state(n_layers, widths, layout, e, next);
+    if (rc != MLP_OK)
+        return rc;
+    hipError_t err = hipMemcpyAsync(next.image, host.data(), next.bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
     if (err == hipSuccess)
         err = hipStreamSynchronize((hipStream_t)stream);
     if (err != hipSuccess) {
         (void)hipFree(next.image);
         return hip_fail(err, "uploading the weight image");
     }
-    next.packed = true;
-    if (g_net.packed)
-        (void)hipFree(g_net.image);
-    g_net = next;
+    commit_state(next);
+    return ok();
+}
+
+int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *const *d_weights,
+                            const void *const *d_biases, int layout, void *stream)
+{
+    const KernelEntry *e = nullptr;
+    int rc = plan(n_layers, widths, layout, &e);
+    if (rc == MLP_OK)
+        rc = check_weights(n_layers, (const uint16_t *const *)d_weights, (const uint16_t *const *)d_biases);
+    if (rc != MLP_OK)
+        return rc;
+    for (int l = 0; l < n_layers; ++l)
+        if (((uintptr_t)d_weights[l] | (uintptr_t)d_biases[l]) & 1)
+            return fail(MLP_ERR_INVALID_ARGUMENT, "d_weights[%d] or d_biases[%d] is not 2-byte aligned", l, l);
+    mlpk::PackArgs args{};
+    mlpk::fill_pack_args(n_layers, widths, e->widths, layout, args);
+    for (int l = 0; l < n_layers; ++l) {
+        args.w[l] = (const uint16_t *)d_weights[l];
+        args.b[l] = (const uint16_t *)d_biases[l];
+    }
+
+    State next;
+    rc = new_state(n_layers, widths, layout, e, next);
+    if (rc != MLP_OK)
+        return rc;
+    args.dst = (uint8_t *)next.image;
+    const hipError_t err = mlpk::launch_pack(args, n_layers, (hipStream_t)stream);
+    if (err != hipSuccess) {
+        (void)hipFree(next.image);
+        return hip_fail(err, "launching the device packer");
+    }
+    commit_state(next);
     return ok();
 }
 

@@ -1,6 +1,7 @@
 // mlp_pack.h -- host-side construction of the device weight images (see mlp_layout.h).
 #pragma once
 
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -16,5 +17,24 @@ size_t image_bytes(int n_layers, const int *kernel_widths, int layout);
 // kernel_widths (each >= the caller's width; the excess is zero).  dst must hold image_bytes().
 void pack_image(int n_layers, const int *widths, const int *kernel_widths, const uint16_t *const *weights,
                 const uint16_t *const *biases, int layout, uint8_t *dst);
+
+// Everything the device packer needs, per layer l (kernel argument, passed by value).  first[l] is
+// the number of work items of the first section (packed: A-fragment slices; row-major: 16-byte
+// chunks of W), items[l] the total; a_off / b_off are the byte offsets of the two sections.
+struct PackArgs {
+    const uint16_t *w[8];
+    const uint16_t *b[8];
+    int win[8], wout[8], mt[8], kb[8];
+    uint32_t a_off[8], b_off[8], first[8], items[8];
+    int layout;
+    uint8_t *dst;
+};
+
+// Fill everything but w, b and dst for the caller's widths and the kernel's widths kw.
+void fill_pack_args(int n_layers, const int *widths, const int *kw, int layout, PackArgs &p);
+
+// Enqueue the device packer on `stream`: it writes the image pack_image would write, from device
+// copies of the weights (p.w, p.b) into p.dst.
+hipError_t launch_pack(const PackArgs &p, int n_layers, hipStream_t stream);
 
 }  // namespace mlpk

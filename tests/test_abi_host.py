@@ -67,6 +67,30 @@ def test_null_arguments_are_rejected():
     assert L.mlp_pack_host(1, w.ctypes.data, ws.wp, ws.bp, 1, dst.ctypes.data, 16) == B.MLP_ERR_INVALID_ARGUMENT
 
 
+def test_device_pack_validation():
+    L = B.lib()
+    w = np.array([4, 4], np.int32)
+    null = (ctypes.c_void_p * 1)(0)
+    good = (ctypes.c_void_p * 1)(0x10000)
+    odd = (ctypes.c_void_p * 1)(0x10001)
+    assert L.mlp_pack_weights_device(1, w.ctypes.data, None, good, 1, None) == B.MLP_ERR_INVALID_ARGUMENT
+    assert L.mlp_pack_weights_device(1, w.ctypes.data, null, good, 1, None) == B.MLP_ERR_INVALID_ARGUMENT
+    assert L.mlp_pack_weights_device(1, w.ctypes.data, good, odd, 1, None) == B.MLP_ERR_INVALID_ARGUMENT
+    assert "aligned" in B.mlp_last_error()
+    assert L.mlp_pack_weights_device(0, w.ctypes.data, good, good, 1, None) == B.MLP_ERR_INVALID_ARGUMENT
+    # row-major is compiled for the dedicated shapes only
+    w3 = np.array([5, 7, 3], np.int32)
+    two = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    assert L.mlp_pack_weights_device(2, w3.ctypes.data, two, two, B.MLP_LAYOUT_ROW_MAJOR, None) == B.MLP_ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(_have_gpu(), reason="checks the error path taken when no GPU is visible")
+def test_device_pack_without_a_device_reports_hip_error():
+    with pytest.raises(B.MlpError) as e:
+        B.mlp_pack_weights_device([0x10000], [0x20000], [4, 4])
+    assert e.value.code == B.MLP_ERR_HIP
+
+
 def test_infer_before_pack_and_bad_batch():
     B.mlp_release()
     B.mlp_release()  # idempotent
