@@ -309,6 +309,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="page", help="workload name or alias (default: page)")
     ap.add_argument("--no-variants", action="store_true", help="skip the row-major / scalarised A/B")
+    ap.add_argument("--layout", choices=("packed", "rowmajor"), default="packed",
+                    help="weight layout of the headline measurement (default: packed)")
     ap.add_argument("--cpu-rows", type=int, default=65536, help="rows of the CPU-oracle sample (0: skip)")
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload table")
     ap.add_argument("--protocol-child", action="store_true", help=argparse.SUPPRESS)
@@ -370,11 +372,13 @@ def main() -> int:
     t0 = time.perf_counter()
     B.mlp_pack_weights(Ws, bs, B.MLP_LAYOUT_PACKED, sh)
     pack_ms = (time.perf_counter() - t0) * 1e3
-    kernel = B.mlp_kernel_name(B.MLP_ACT_VECTOR)
     pack = {"host_ms": round(pack_ms, 4), "device_kernel_ms": round(measure_device_pack(torch, B, wl, Ws, bs), 6),
             "note": "host_ms: host packing + upload + synchronisation (wall clock); device_kernel_ms: the "
                     "conversion kernel of mlp_pack_weights_device from device-resident weights (HIP events "
                     "with the queue kept busy ahead, median of 10); the page quotes ~0.0086 ms for its conversion on its own GPU"}
+    layout = B.MLP_LAYOUT_PACKED if args.layout == "packed" else B.MLP_LAYOUT_ROW_MAJOR
+    B.mlp_pack_weights(Ws, bs, layout, sh)
+    kernel = B.mlp_kernel_name(B.MLP_ACT_VECTOR)
 
     def step():
         B.mlp_infer_ex(wl.batch, x.data_ptr(), y.data_ptr(), sh, B.MLP_ACT_VECTOR)
@@ -438,7 +442,7 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": wl.name, "widths": list(wl.widths), "batch": wl.batch,
-                   "unique_inputs": wl.unique_rows, "replicas": wl.replicas, "layout": "packed",
+                   "unique_inputs": wl.unique_rows, "replicas": wl.replicas, "layout": args.layout,
                    "activation": "vector", "flops_per_eval": wl.flops_per_eval},
         "frac_fp16_peak": roofline["frac"],
         "pack_ms": round(pack_ms, 4),

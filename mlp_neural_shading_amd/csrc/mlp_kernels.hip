@@ -119,7 +119,7 @@ struct Body {
             // the rows are padded (mlp_layout.h), in global memory they are as given.
             constexpr int win = N::w[l], wout = N::w[l + 1];
             static_assert(win % 8 == 0, "row-major layers need w_in % 8 == 0");
-            constexpr int stride = LDS_W ? mlpl::rml_stride(win) : win * 2;
+            constexpr int stride = LDS_W ? mlpl::rml_stride(l, win) : win * 2;
             constexpr int w_off = LDS_W ? (int)mlpl::rml_w_off(N::w, l) : (int)mlpl::rm_w_off(N::w, l);
             const int g = lane >> 5, m = lane & 31;
             const int r = 32 * mt + m;
@@ -413,21 +413,28 @@ __device__ __forceinline__ int rowmajor_lds_offset(int g, std::integer_sequence<
         constexpr int w0 = (int)mlpl::rm_w_off(N::w, l), b0 = (int)mlpl::rm_b_off(N::w, l);
         constexpr int end = (int)mlpl::rm_w_off(N::w, l + 1), row = N::w[l] * 2;
         if (g >= w0 && g < end)
-            o = g < b0 ? (int)mlpl::rml_w_off(N::w, l) + (g - w0) / row * mlpl::rml_stride(N::w[l]) + (g - w0) % row
+            o = g < b0 ? (int)mlpl::rml_w_off(N::w, l) + (g - w0) / row * mlpl::rml_stride(l, N::w[l]) + (g - w0) % row
                        : (int)mlpl::rml_b_off(N::w, l) + (g - b0);
     };
     (one(std::integral_constant<int, L>()), ...);
     return o;
 }
 
-// Stage a row-major image into LDS with padded rows (same load pattern as stage_image).
+// Stage a row-major image into LDS with padded rows (same load pattern as stage_image).  Padded rows
+// are only 8-byte aligned, so each 16-byte chunk is stored as two 8-byte halves.
+__device__ __forceinline__ void store_chunk8(uint8_t *dst, const uint4 &v)
+{
+    ((uint2 *)dst)[0] = make_uint2(v.x, v.y);
+    ((uint2 *)dst)[1] = make_uint2(v.z, v.w);
+}
+
 template <class N, int BYTES, int THREADS, int... K>
 __device__ __forceinline__ void stage_rowmajor(uint8_t *lds, const uint8_t *image, std::integer_sequence<int, K...>)
 {
     const int t16 = (int)threadIdx.x * 16;
     const uint4 v[] = {*(const uint4 *)(image + (K * THREADS * 16 + t16 < BYTES ? K * THREADS * 16 + t16 : BYTES - 16))...};
     ((K * THREADS * 16 + t16 < BYTES
-          ? (void)(*(uint4 *)(lds + rowmajor_lds_offset<N>(K * THREADS * 16 + t16, std::make_integer_sequence<int, N::L>())) = v[K])
+          ? store_chunk8(lds + rowmajor_lds_offset<N>(K * THREADS * 16 + t16, std::make_integer_sequence<int, N::L>()), v[K])
           : (void)0),
      ...);
 }

@@ -74,13 +74,17 @@ constexpr size_t rm_w_off(const int *w, int l)
 constexpr size_t rm_b_off(const int *w, int l) { return rm_w_off(w, l) + rm_w_bytes(w, l); }
 constexpr size_t rm_bytes(const int *w, int L) { return rm_w_off(w, L); }
 
-// Row-major image as staged in LDS: the same matrices, each row padded by 16 bytes.  A fragment read
-// touches 16 consecutive rows at once; with a row stride of w_in * 2 + 16 bytes (w_in a multiple of
-// 8) the rows start 4 (mod 64) banks apart, so the 16 rows fall in distinct groups of four banks
-// ("Optimization Techniques", "Avoiding Bank Conflicts": pad the row stride).  Unpadded, a 64-wide
-// layer's 128-byte rows all start in the same bank.
-constexpr int rml_stride(int win) { return win * 2 + 16; }
-constexpr size_t rml_w_bytes(const int *w, int l) { return (size_t)w[l + 1] * rml_stride(w[l]); }
+// Row-major image as staged in LDS: the same matrices with padded rows ("Optimization Techniques",
+// "Avoiding Bank Conflicts": pad the row stride), so that the 32 rows one fragment read touches
+// fall in distinct LDS banks (64 banks of 4 bytes).  Unpadded, a 64-wide layer's 128-byte rows all
+// start in the same bank.  Widths are multiples of 8.
+//   layer 0: each lane reads 16 bytes (ds_read_b128, 16-byte aligned); stride w_in * 2 + 16 bytes
+//            puts consecutive rows 4 banks apart (mod 64), so every 16 rows cover the 64 banks once;
+//   layers >= 1: each lane reads 8 bytes twice (ds_read_b64); stride w_in * 2 + 8 bytes is 2 x an
+//            odd number of banks, so the 32 rows start on 32 distinct even banks and cover all 64.
+// Every section starts on a 16-byte boundary; rows of layers >= 1 are 8-byte aligned.
+constexpr int rml_stride(int l, int win) { return win * 2 + (l == 0 ? 16 : 8); }
+constexpr size_t rml_w_bytes(const int *w, int l) { return (size_t)round_up(w[l + 1] * rml_stride(l, w[l]), 16); }
 constexpr size_t rml_w_off(const int *w, int l)
 {
     size_t o = 0;
