@@ -16,6 +16,7 @@ inference", section "Experiment setup").  Prints one JSON line:
   workloads    every workload (all five network shapes) timed the same way, with the FP16 MFMA and
                the HBM fraction of each
   dispatch     an empty kernel timed the same way, and the wall-clock gap between back-to-back steps
+  overlap      mlp_infer on a second stream beside a copy or a GEMM: alone, serial and concurrent times
   clocks       the GPU clocks reported by rocm-smi before and after the measurements
   cpu_baseline the CPU oracle on a bounded sample of the same rows, one host thread pinned to a core
 """
@@ -191,6 +192,64 @@ def measure_workloads(torch, B, workloads, skip: str) -> dict:
     return res
 
 
+def measure_overlap(torch, B, wl, x, y) -> dict:
+    """mlp_infer on its own stream beside a background workload on another stream (both at the default
+    priority), against each alone and one after the other: the gap-filling of running them together.
+    Backgrounds: a 512 MiB device copy (HBM-bound) and a 4096^3 FP16 matrix product (MFMA-bound).
+    Times are HIP events: the earliest start to the latest end, median of 5."""
+    dev = torch.device("cuda:0")
+    s_mlp = torch.cuda.Stream(device=dev)
+    s_bg = torch.cuda.Stream(device=dev)
+    src = torch.empty(256 * 1024 * 1024, dtype=torch.float16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    a = torch.randn(4096, 4096, device=dev).to(torch.float16)
+    bm = torch.randn(4096, 4096, device=dev).to(torch.float16)
+    c = torch.empty(4096, 4096, dtype=torch.float16, device=dev)
+    backgrounds = {"copy_512MiB": lambda: dst.copy_(src), "gemm_fp16_4096": lambda: torch.matmul(a, bm, out=c)}
+    reps = 4  # back-to-back calls of each side per measurement
+
+    def mlp():
+        for _ in range(reps):
+            B.mlp_infer(wl.batch, x.data_ptr(), y.data_ptr(), s_mlp.cuda_stream)
+
+    def timed(run_mlp, run_bg, together):
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        ends = []
+        start.record(torch.cuda.current_stream())
+        for st, fn in ((s_mlp, run_mlp), (s_bg, run_bg)):
+            if fn is None:
+                continue
+            st.wait_stream(torch.cuda.current_stream())
+            if not together and ends:
+                st.wait_event(ends[-1])
+            with torch.cuda.stream(st):
+                fn()
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(st)
+            ends.append(e)
+        torch.cuda.synchronize()
+        return max(start.elapsed_time(e) for e in ends)
+
+    res = {"calls_per_side": reps}
+    for name, bg in backgrounds.items():
+        def bg_run(bg=bg):
+            for _ in range(reps):
+                bg()
+        for _ in range(2):
+            timed(mlp, bg_run, True)
+        alone_mlp = statistics.median(timed(mlp, None, False) for _ in range(5))
+        alone_bg = statistics.median(timed(None, bg_run, False) for _ in range(5))
+        serial = statistics.median(timed(mlp, bg_run, False) for _ in range(5))
+        together = statistics.median(timed(mlp, bg_run, True) for _ in range(5))
+        res[name] = {"mlp_alone_ms": round(alone_mlp, 4), "background_alone_ms": round(alone_bg, 4),
+                     "serial_ms": round(serial, 4), "concurrent_ms": round(together, 4),
+                     "saved_frac": round(1 - together / serial, 4)}
+    del src, dst, a, bm, c
+    torch.cuda.empty_cache()
+    return res
+
+
 def read_clocks() -> dict:
     """Current SCLK / MCLK as rocm-smi reports them (best effort; the clocks cannot be locked here)."""
     import subprocess
@@ -313,6 +372,7 @@ def main() -> int:
                     help="weight layout of the headline measurement (default: packed)")
     ap.add_argument("--cpu-rows", type=int, default=65536, help="rows of the CPU-oracle sample (0: skip)")
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--no-overlap", action="store_true", help="skip the two-stream overlap measurement")
     ap.add_argument("--protocol-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--layout-order", default="01", help=argparse.SUPPRESS)
     ap.add_argument("--no-ceiling", action="store_true", help="skip the random-operand MFMA ceiling probe")
@@ -418,6 +478,10 @@ def main() -> int:
         c = ceiling["valu_per_mfma_0"]["tflops"]
         roofline["frac_of_measured_ceiling"] = round(achieved_tflops / c, 4)
 
+    overlap = None
+    if not args.no_overlap:
+        overlap = measure_overlap(torch, B, wl, x, y)
+
     per_workload = {}
     if not args.no_workloads:
         per_workload = measure_workloads(torch, B, workloads, skip=wl.name)
@@ -450,6 +514,7 @@ def main() -> int:
         "roofline": roofline,
         "variants": variants,
         "dispatch": dispatch,
+        "overlap": overlap,
         "workloads": per_workload,
         "clocks": {"before": clocks_before, "after": clocks_after,
                    "note": "clocks are not locked on this machine; the kernel-side clock of the ceiling probe "
