@@ -17,6 +17,7 @@ inference", section "Experiment setup").  Prints one JSON line:
                the HBM fraction of each
   dispatch     an empty kernel timed the same way, and the wall-clock gap between back-to-back steps
   overlap      mlp_infer on a second stream beside a copy or a GEMM: alone, serial and concurrent times
+  layered      networks beyond the fused kernels (widths > 128, more than 8 layers), layer by layer
   clocks       the GPU clocks reported by rocm-smi before and after the measurements
   cpu_baseline the CPU oracle on a bounded sample of the same rows, one host thread pinned to a core
 """
@@ -246,6 +247,33 @@ def measure_overlap(torch, B, wl, x, y) -> dict:
                      "serial_ms": round(serial, 4), "concurrent_ms": round(together, 4),
                      "saved_frac": round(1 - together / serial, 4)}
     del src, dst, a, bm, c
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_layered(torch, B, workloads) -> dict:
+    """Networks beyond the fused kernels (one MFMA GEMM per layer with the fused epilogue): median of
+    10 event-timed dispatches after 3 warm-ups, FLOPs = 2 * sum w_{l-1} w_l per row."""
+    res = {}
+    dev = torch.device("cuda:0")
+    sh = torch.cuda.current_stream().cuda_stream
+    for widths, rows in (((64,) + (1024,) * 7 + (16,), 65536), ((256,) * 17, 262144)):
+        Ws, bs = workloads.init_weights(widths, seed=1)
+        gen = torch.Generator(device=dev).manual_seed(3)
+        x = (torch.rand((rows, widths[0]), device=dev, generator=gen) * 2 - 1).to(torch.float16)
+        y = torch.empty((rows, widths[-1]), dtype=torch.float16, device=dev)
+        B.mlp_pack_weights(Ws, bs, B.MLP_LAYOUT_PACKED, sh)
+        f = lambda: B.mlp_infer(rows, x.data_ptr(), y.data_ptr(), sh)
+        for _ in range(3):
+            f()
+        ms = statistics.median(time_dispatches(torch, f, 10))
+        flops = 2 * rows * sum(widths[l] * widths[l + 1] for l in range(len(widths) - 1))
+        tflops = flops / (ms * 1e-3) / 1e12
+        name = "mlp%d-%s-b%d" % (len(widths) - 1, "-".join(str(w) for w in widths), rows)
+        res[name] = {"median_ms": round(ms, 4), "m_evals_per_s": round(throughput_m_evals(rows, ms), 1),
+                     "tflops": round(tflops, 1), "frac_fp16_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
+                     "kernel": B.mlp_kernel_name(B.MLP_ACT_VECTOR)}
+        del x, y
     torch.cuda.empty_cache()
     return res
 
@@ -483,9 +511,11 @@ def main() -> int:
         overlap = measure_overlap(torch, B, wl, x, y)
 
     per_workload = {}
+    layered = {}
     if not args.no_workloads:
         per_workload = measure_workloads(torch, B, workloads, skip=wl.name)
         per_workload[wl.name]["variants"] = variants
+        layered = measure_layered(torch, B, workloads)
     clocks_after = read_clocks()
 
     cpu = None
@@ -516,6 +546,7 @@ def main() -> int:
         "dispatch": dispatch,
         "overlap": overlap,
         "workloads": per_workload,
+        "layered": layered,
         "clocks": {"before": clocks_before, "after": clocks_after,
                    "note": "clocks are not locked on this machine; the kernel-side clock of the ceiling probe "
                            "is in roofline.measured_ceiling"},

@@ -52,8 +52,13 @@ enum {
     MLP_ACT_SCALARISED = 1 /* one component at a time: if (v < 0) v *= half(0.01)                */
 };
 
-#define MLP_MAX_LAYERS 8
-#define MLP_MAX_WIDTH 128
+#define MLP_MAX_LAYERS 64  /* any network up to 64 layers ...                                  */
+#define MLP_MAX_WIDTH 4096 /* ... of widths up to 4096 (see MLP_FUSED_*)                         */
+/* Networks within these limits run as one fused kernel (weights in LDS, activations in registers);
+ * wider or deeper ones run layer by layer (one MFMA GEMM with the fused epilogue per layer, the
+ * activations between layers in device memory), packed layout and vector activation only. */
+#define MLP_FUSED_MAX_LAYERS 8
+#define MLP_FUSED_MAX_WIDTH 128
 
 /* Size in bytes of the device image mlp_pack_weights would build for this shape and layout.
  *   n_layers  number of affine layers, 1..MLP_MAX_LAYERS
@@ -61,13 +66,15 @@ enum {
  *             each 1..MLP_MAX_WIDTH
  *   layout    MLP_LAYOUT_ROW_MAJOR or MLP_LAYOUT_PACKED
  *   out_bytes receives the size
- * Host only; no HIP call.  MLP_ERR_UNSUPPORTED for a row-major request on a shape that only the
- * generic (packed) kernel serves. */
+ * Host only; no HIP call.  MLP_ERR_UNSUPPORTED for a row-major request on a shape that no dedicated
+ * kernel serves (generic fused shapes and layer-by-layer shapes take the packed layout only). */
 int mlp_packed_size(int n_layers, const int32_t *widths, int layout, size_t *out_bytes);
 
 /* The widths the selected kernel computes with (input width padded as the kernel reads it, every
  * layer width padded to its tile multiple): kernel_widths receives n_layers + 1 entries.  Shapes
- * without a dedicated kernel run on a generic kernel whose widths are all MLP_MAX_WIDTH, zero-padded.
+ * without a dedicated kernel but within the fused limits run on a generic fused kernel whose widths
+ * are all MLP_FUSED_MAX_WIDTH, zero-padded; wider or deeper shapes run layer by layer with the input
+ * width padded to a multiple of 32 and every layer width to a multiple of 128.
  * Host only; no HIP call. */
 int mlp_plan_widths(int n_layers, const int32_t *widths, int layout, int32_t *kernel_widths);
 
@@ -110,7 +117,11 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
  *   out_ptr  device pointer, [batch][widths[n_layers]] FP16 row-major, 16-byte aligned, must not
  *            overlap in_ptr
  *   stream   hipStream_t (NULL = the default stream)
- * Asynchronous: the buffers must stay valid until the stream's work completes.  Must be called
+ * Asynchronous: the buffers must stay valid until the stream's work completes.  A network beyond the
+ * fused limits runs as one kernel per layer over blocks of 65,536 rows, its intermediate activations
+ * in two scratch buffers (rows x the widest hidden width, padded to 32, FP16) that the call
+ * allocates and frees in order on `stream` from a memory pool the library keeps (so calls on
+ * different streams never share them); MLP_ERR_OUT_OF_MEMORY if they cannot be allocated.  Must be called
  * with the device that was current at pack time.  Uses the activation form set by
  * mlp_set_activation_mode (default MLP_ACT_VECTOR).  Concurrent calls on different streams are
  * safe (the weights are read-only).  A device fault, should one occur, surfaces at the caller's

@@ -26,8 +26,10 @@ MLP_LAYOUT_ROW_MAJOR = 0
 MLP_LAYOUT_PACKED = 1
 MLP_ACT_VECTOR = 0
 MLP_ACT_SCALARISED = 1
-MLP_MAX_LAYERS = 8
-MLP_MAX_WIDTH = 128
+MLP_MAX_LAYERS = 64
+MLP_MAX_WIDTH = 4096
+MLP_FUSED_MAX_LAYERS = 8
+MLP_FUSED_MAX_WIDTH = 128
 
 EXPORTED = (
     "mlp_packed_size", "mlp_plan_widths", "mlp_pack_host", "mlp_pack_weights", "mlp_pack_weights_device",

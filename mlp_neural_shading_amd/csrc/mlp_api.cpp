@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "mlp.h"
+#include "mlp_layered.h"
 #include "mlp_layout.h"
 #include "mlp_pack.h"
 #include "mlp_registry.h"
@@ -58,6 +59,49 @@ struct State {
 State g_net;
 int g_act_mode = MLP_ACT_VECTOR;
 
+// The layer-by-layer path (mlp_layered.hip) stands in the registry's place for shapes no fused kernel
+// serves: widths above MLP_FUSED_MAX_WIDTH or more than MLP_FUSED_MAX_LAYERS layers.
+const KernelEntry kLayered = {"mlp_layered<gemm 128x128, fused epilogue>", 0, {}, true, MLP_LAYOUT_PACKED,
+                              MLP_ACT_VECTOR, 256, 128, true, nullptr, nullptr};
+bool is_layered(const KernelEntry *e) { return e == &kLayered; }
+
+// Rows per pass of the layered path (its scratch holds two such blocks of activations).
+constexpr int64_t kLayeredChunkRows = 65536;
+
+// Device memory for the layered path's intermediate activations: a pool owned by the library with
+// no release threshold, so that the stream-ordered allocation of each call reuses memory.
+hipMemPool_t g_pool = nullptr;
+int g_pool_device = -1;
+
+int layered_pool(int device, hipMemPool_t *out)
+{
+    if (!g_pool || g_pool_device != device) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = device;
+        hipMemPool_t pool = nullptr;
+        hipError_t err = hipMemPoolCreate(&pool, &props);
+        if (err != hipSuccess)
+            return hip_fail(err, "hipMemPoolCreate");
+        uint64_t keep = UINT64_MAX;
+        err = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (err != hipSuccess) {
+            (void)hipMemPoolDestroy(pool);
+            return hip_fail(err, "hipMemPoolSetAttribute(release threshold)");
+        }
+        g_pool = pool;  // a pool made for another device is kept: its memory may still be in use
+        g_pool_device = device;
+    }
+    *out = g_pool;
+    return MLP_OK;
+}
+
+size_t state_image_bytes(int n_layers, const int32_t *widths, int layout, const KernelEntry *e)
+{
+    return is_layered(e) ? mlpk::layered_image_bytes(n_layers, widths) : mlpk::image_bytes(n_layers, e->widths, layout);
+}
+
 int check_shape(int n_layers, const int32_t *widths)
 {
     if (n_layers < 1 || n_layers > MLP_MAX_LAYERS)
@@ -85,7 +129,8 @@ int check_act(int act)
 }
 
 // The instance that serves (shape, layout, act): an exact-shape instance, else for the packed
-// layout with the vector activation the generic instance for that layer count, else none.
+// layout with the vector activation and widths within the fused limits the generic instance for
+// that layer count, else none.
 const KernelEntry *select(int n_layers, const int32_t *widths, int layout, int act)
 {
     int count = 0;
@@ -102,6 +147,9 @@ const KernelEntry *select(int n_layers, const int32_t *widths, int layout, int a
     }
     if (layout != MLP_LAYOUT_PACKED || act != MLP_ACT_VECTOR)
         return nullptr;
+    for (int k = 0; k <= n_layers; ++k)
+        if (widths[k] > MLP_FUSED_MAX_WIDTH)
+            return nullptr;  // beyond the generic kernels
     for (int i = 0; i < count; ++i)
         if (all[i].generic && all[i].n_layers == n_layers)
             return &all[i];
@@ -116,6 +164,8 @@ int plan(int n_layers, const int32_t *widths, int layout, const KernelEntry **ou
     if (rc != MLP_OK)
         return rc;
     const KernelEntry *e = select(n_layers, widths, layout, MLP_ACT_VECTOR);
+    if (!e && layout == MLP_LAYOUT_PACKED)
+        e = &kLayered;  // wider or deeper than the fused kernels
     if (!e)
         return fail(MLP_ERR_UNSUPPORTED, "no kernel serves this shape with the %s layout (row-major is "
                     "compiled for the dedicated shapes only)", layout == MLP_LAYOUT_PACKED ? "packed" : "row-major");
@@ -145,7 +195,7 @@ int mlp_packed_size(int n_layers, const int32_t *widths, int layout, size_t *out
     const int rc = plan(n_layers, widths, layout, &e);
     if (rc != MLP_OK)
         return rc;
-    *out_bytes = mlpk::image_bytes(n_layers, e->widths, layout);
+    *out_bytes = state_image_bytes(n_layers, widths, layout, e);
     return ok();
 }
 
@@ -157,6 +207,12 @@ int mlp_plan_widths(int n_layers, const int32_t *widths, int layout, int32_t *ke
     const int rc = plan(n_layers, widths, layout, &e);
     if (rc != MLP_OK)
         return rc;
+    if (is_layered(e)) {
+        kernel_widths[0] = mlpk::layered_kin(widths[0]);
+        for (int l = 1; l <= n_layers; ++l)
+            kernel_widths[l] = mlpk::layered_kout(widths[l]);
+        return ok();
+    }
     kernel_widths[0] = mlpl::k0_pad(e->widths[0]);
     for (int l = 1; l <= n_layers; ++l)
         kernel_widths[l] = mlpl::round_up(e->widths[l], mlpl::kTileM);
@@ -172,12 +228,15 @@ int mlp_pack_host(int n_layers, const int32_t *widths, const uint16_t *const *we
         rc = check_weights(n_layers, weights, biases);
     if (rc != MLP_OK)
         return rc;
-    const size_t need = mlpk::image_bytes(n_layers, e->widths, layout);
+    const size_t need = state_image_bytes(n_layers, widths, layout, e);
     if (!host_dst)
         return fail(MLP_ERR_INVALID_ARGUMENT, "host_dst is NULL");
     if (dst_bytes < need)
         return fail(MLP_ERR_INVALID_ARGUMENT, "host_dst holds %zu bytes, the image needs %zu", dst_bytes, need);
-    mlpk::pack_image(n_layers, widths, e->widths, weights, biases, layout, (uint8_t *)host_dst);
+    if (is_layered(e))
+        mlpk::pack_layered(n_layers, widths, weights, biases, (uint8_t *)host_dst);
+    else
+        mlpk::pack_image(n_layers, widths, e->widths, weights, biases, layout, (uint8_t *)host_dst);
     return ok();
 }
 
@@ -193,8 +252,8 @@ int new_state(int n_layers, const int32_t *widths, int layout, const KernelEntry
         next.widths[i] = widths[i];
     next.layout = layout;
     next.entry[MLP_ACT_VECTOR] = e;
-    next.entry[MLP_ACT_SCALARISED] = select(n_layers, widths, layout, MLP_ACT_SCALARISED);
-    next.bytes = mlpk::image_bytes(n_layers, e->widths, layout);
+    next.entry[MLP_ACT_SCALARISED] = is_layered(e) ? nullptr : select(n_layers, widths, layout, MLP_ACT_SCALARISED);
+    next.bytes = state_image_bytes(n_layers, widths, layout, e);
     hipError_t err = hipGetDevice(&next.device);
     if (err != hipSuccess)
         return hip_fail(err, "hipGetDevice");
@@ -204,7 +263,7 @@ int new_state(int n_layers, const int32_t *widths, int layout, const KernelEntry
         return hip_fail(err, "hipDeviceGetAttribute(multiProcessorCount)");
     for (int a = 0; a < 2; ++a) {
         const KernelEntry *k = next.entry[a];
-        if (!k)
+        if (!k || is_layered(k))
             continue;
         int blocks = 0;
         err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k->func, k->threads, 0);
@@ -244,8 +303,11 @@ int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const 
         rc = check_weights(n_layers, weights, biases);
     if (rc != MLP_OK)
         return rc;
-    std::vector<uint8_t> host(mlpk::image_bytes(n_layers, e->widths, layout));
-    mlpk::pack_image(n_layers, widths, e->widths, weights, biases, layout, host.data());
+    std::vector<uint8_t> host(state_image_bytes(n_layers, widths, layout, e));
+    if (is_layered(e))
+        mlpk::pack_layered(n_layers, widths, weights, biases, host.data());
+    else
+        mlpk::pack_image(n_layers, widths, e->widths, weights, biases, layout, host.data());
 
     State next;
     rc = new_state(n_layers, widths, layout, e, next);
@@ -274,26 +336,100 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
     for (int l = 0; l < n_layers; ++l)
         if (((uintptr_t)d_weights[l] | (uintptr_t)d_biases[l]) & 1)
             return fail(MLP_ERR_INVALID_ARGUMENT, "d_weights[%d] or d_biases[%d] is not 2-byte aligned", l, l);
-    mlpk::PackArgs args{};
-    mlpk::fill_pack_args(n_layers, widths, e->widths, layout, args);
-    for (int l = 0; l < n_layers; ++l) {
-        args.w[l] = (const uint16_t *)d_weights[l];
-        args.b[l] = (const uint16_t *)d_biases[l];
-    }
-
     State next;
     rc = new_state(n_layers, widths, layout, e, next);
     if (rc != MLP_OK)
         return rc;
-    args.dst = (uint8_t *)next.image;
-    const hipError_t err = mlpk::launch_pack(args, n_layers, (hipStream_t)stream);
-    if (err != hipSuccess) {
-        (void)hipFree(next.image);
-        return hip_fail(err, "launching the device packer");
+    // The conversion kernel takes up to 8 layers per launch.
+    for (int l0 = 0; l0 < n_layers; l0 += 8) {
+        const int count = n_layers - l0 < 8 ? n_layers - l0 : 8;
+        mlpk::PackArgs args{};
+        if (is_layered(e))
+            mlpk::fill_pack_args_layered(widths, l0, count, args);
+        else
+            mlpk::fill_pack_args(n_layers, widths, e->widths, layout, args);
+        for (int i = 0; i < count; ++i) {
+            args.w[i] = (const uint16_t *)d_weights[l0 + i];
+            args.b[i] = (const uint16_t *)d_biases[l0 + i];
+        }
+        args.dst = (uint8_t *)next.image;
+        const hipError_t err = mlpk::launch_pack(args, count, (hipStream_t)stream);
+        if (err != hipSuccess) {
+            (void)hipFree(next.image);
+            return hip_fail(err, "launching the device packer");
+        }
     }
     commit_state(next);
     return ok();
 }
+
+}  // extern "C"
+
+namespace {
+
+// The layered path: rows in blocks of kLayeredChunkRows, each block through every layer, with the
+// activations between layers in two scratch buffers allocated on the stream (stream-ordered, so
+// calls on different streams never share them) and freed on it afterwards.
+int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t stream)
+{
+    const int L = g_net.n_layers;
+    const int *w = g_net.widths;
+    int ld_max = 0;  // row stride of the scratch buffers: the widest hidden layer, padded to 32 halves
+    for (int l = 1; l < L; ++l)
+        ld_max = mlpk::layered_kin(w[l]) > ld_max ? mlpk::layered_kin(w[l]) : ld_max;
+    const int64_t chunk = batch < kLayeredChunkRows ? batch : kLayeredChunkRows;
+    void *buf[2] = {nullptr, nullptr};
+    if (L > 1) {
+        hipMemPool_t pool = nullptr;
+        const int rc = layered_pool(g_net.device, &pool);
+        if (rc != MLP_OK)
+            return rc;
+        const size_t bytes = (size_t)chunk * ld_max * 2;
+        for (int i = 0; i < (L > 2 ? 2 : 1); ++i) {
+            const hipError_t err = hipMallocFromPoolAsync(&buf[i], bytes, pool, stream);
+            if (err != hipSuccess) {
+                if (buf[0])
+                    (void)hipFreeAsync(buf[0], stream);
+                const int code = err == hipErrorOutOfMemory ? MLP_ERR_OUT_OF_MEMORY : MLP_ERR_HIP;
+                return fail(code, "hipMallocFromPoolAsync(%zu) failed: %s", bytes, hipGetErrorString(err));
+            }
+        }
+    }
+    hipError_t err = hipSuccess;
+    for (int64_t r0 = 0; r0 < batch && err == hipSuccess; r0 += chunk) {
+        const int64_t rows = batch - r0 < chunk ? batch - r0 : chunk;
+        for (int l = 0; l < L && err == hipSuccess; ++l) {
+            mlpk::LayerArgs a{};
+            a.x = l == 0 ? (const uint16_t *)in_ptr + r0 * w[0] : (const uint16_t *)buf[(l - 1) & 1];
+            a.ldx = l == 0 ? w[0] : ld_max;
+            a.y = l == L - 1 ? (uint16_t *)out_ptr + r0 * w[L] : (uint16_t *)buf[l & 1];
+            a.ldy = l == L - 1 ? w[L] : ld_max;
+            const size_t off = mlpk::layered_layer_offset(w, l);
+            a.a = (const uint8_t *)g_net.image + off;
+            a.bias = (const float *)((const uint8_t *)g_net.image + off + mlpk::layered_a_bytes(w[l], w[l + 1]));
+            a.rows = rows;
+            a.row_tiles = (rows + mlpk::layered_rows_per_tile() - 1) / mlpk::layered_rows_per_tile();
+            a.win = w[l];
+            a.wout = w[l + 1];
+            a.kin = mlpk::layered_kin(w[l]);
+            a.kout = mlpk::layered_kout(w[l + 1]);
+            a.act = l + 1 < L;
+            a.vec_x = a.ldx % 8 == 0 && ((uintptr_t)a.x & 15) == 0;
+            a.vec_y = a.ldy % 4 == 0 && ((uintptr_t)a.y & 7) == 0;
+            err = mlpk::launch_layer(a, stream);
+        }
+    }
+    for (int i = 0; i < 2; ++i)
+        if (buf[i])
+            (void)hipFreeAsync(buf[i], stream);
+    if (err != hipSuccess)
+        return hip_fail(err, "layer kernel launch");
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
 
 int mlp_infer_ex(int64_t batch, const void *in_ptr, void *out_ptr, void *stream, int act_mode)
 {
@@ -330,6 +466,8 @@ int mlp_infer_ex(int64_t batch, const void *in_ptr, void *out_ptr, void *stream,
         return fail(MLP_ERR_INVALID_ARGUMENT, "current device %d is not the device %d the network was packed on",
                     dev, g_net.device);
 
+    if (is_layered(e))
+        return infer_layered(batch, in_ptr, out_ptr, (hipStream_t)stream);
     const int64_t rows_per_block = (int64_t)e->rows_per_wave * (e->threads / 64);
     const int64_t blocks = (batch + rows_per_block - 1) / rows_per_block;
     const int grid = (int)(blocks < g_net.grid_cap[act_mode] ? blocks : g_net.grid_cap[act_mode]);

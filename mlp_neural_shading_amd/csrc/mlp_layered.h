@@ -1,0 +1,45 @@
+// mlp_layered.h -- the layer-by-layer path for networks beyond the fused kernels (widths > 128 or
+// more than 8 layers): geometry of its weight image and the per-layer kernel launch.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mlpk {
+
+// Padded widths of the layered image: every layer's K (input width) to a multiple of 32, every
+// layer's M (output width) to a multiple of 128 (the kernel's workgroup tile).
+inline int layered_kin(int w) { return (w + 31) / 32 * 32; }
+inline int layered_kout(int w) { return (w + 127) / 128 * 128; }
+
+// Per layer l, in order: A fragments [kout/32][kin/16][64 lanes][8 halves] (natural K order: slot
+// (kb, g, j) holds input feature 16 kb + 8 g + j), then FP32 bias tiles [kout/32][2][16] (entry
+// (mt, g, j) = b[32 mt + 8 (j / 4) + 4 g + j % 4]).  Zero outside the real matrix.
+inline size_t layered_a_bytes(int win, int wout) { return (size_t)(layered_kout(wout) / 32) * (layered_kin(win) / 16) * 1024; }
+inline size_t layered_b_bytes(int wout) { return (size_t)(layered_kout(wout) / 32) * 128; }
+inline size_t layered_layer_bytes(int win, int wout) { return layered_a_bytes(win, wout) + layered_b_bytes(wout); }
+
+// Everything one layer launch needs (kernel argument, by value).
+struct LayerArgs {
+    const uint16_t *x;  // [rows][ldx] FP16, columns 0..win-1 used
+    int64_t ldx;
+    uint16_t *y;        // [rows][ldy] FP16, columns 0..wout-1 written
+    int64_t ldy;
+    const uint8_t *a;   // this layer's A fragments
+    const float *bias;  // this layer's bias tiles
+    int64_t rows;
+    int64_t row_tiles;  // ceil(rows / 128)
+    int win, wout;      // real widths
+    int kin, kout;      // padded widths (layered_kin / layered_kout)
+    int act;            // 1: leaky ReLU after the rounding; 0: none (last layer)
+    int vec_x;          // 1: rows of x are 16-byte aligned (ldx % 8 == 0, x aligned)
+    int vec_y;          // 1: rows of y are 8-byte aligned (ldy % 4 == 0, y aligned)
+};
+
+hipError_t launch_layer(const LayerArgs &p, hipStream_t stream);
+
+// Rows one workgroup covers (the row tile).
+int layered_rows_per_tile();
+
+}  // namespace mlpk

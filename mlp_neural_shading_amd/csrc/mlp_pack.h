@@ -27,11 +27,21 @@ struct PackArgs {
     int win[8], wout[8], mt[8], kb[8];
     uint32_t a_off[8], b_off[8], first[8], items[8];
     int layout;
+    int natural;  // 1: every layer in natural K order (the layered image), 0: the fused kernels' order
     uint8_t *dst;
 };
 
 // Fill everything but w, b and dst for the caller's widths and the kernel's widths kw.
 void fill_pack_args(int n_layers, const int *widths, const int *kw, int layout, PackArgs &p);
+
+// The layered path's image (mlp_layered.h): bytes, and the host packer.  Layers are packed one after
+// another; layer_offset(l) is where layer l starts.
+size_t layered_image_bytes(int n_layers, const int *widths);
+size_t layered_layer_offset(const int *widths, int l);
+void pack_layered(int n_layers, const int *widths, const uint16_t *const *weights, const uint16_t *const *biases,
+                  uint8_t *dst);
+// Fill args for layers l0 .. l0 + count - 1 (count <= 8) of the layered image (natural K order).
+void fill_pack_args_layered(const int *widths, int l0, int count, PackArgs &p);
 
 // Enqueue the device packer on `stream`: it writes the image pack_image would write, from device
 // copies of the weights (p.w, p.b) into p.dst.

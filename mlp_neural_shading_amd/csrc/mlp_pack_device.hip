@@ -9,6 +9,7 @@
 // (row-major); one thread writes each 64-byte half of a bias tile.
 #include <hip/hip_runtime.h>
 
+#include "mlp_layered.h"
 #include "mlp_layout.h"
 #include "mlp_pack.h"
 
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs p)
                 uint16_t v[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const int f = mlpl::slot_feature(l, kb, g, j);
+                    const int f = p.natural ? 16 * kb + 8 * g + j : mlpl::slot_feature(l, kb, g, j);
                     v[j] = (r < wout && f < win) ? W[(size_t)r * win + f] : 0;
                 }
                 *(uint4 *)(p.dst + p.a_off[l] + (size_t)i * 16) = __builtin_bit_cast(uint4, v);
@@ -67,6 +68,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs p)
 void fill_pack_args(int n_layers, const int *widths, const int *kw, int layout, PackArgs &p)
 {
     p.layout = layout;
+    p.natural = 0;
     for (int l = 0; l < n_layers; ++l) {
         p.win[l] = widths[l];
         p.wout[l] = widths[l + 1];
@@ -83,6 +85,24 @@ void fill_pack_args(int n_layers, const int *widths, const int *kw, int layout, 
             p.first[l] = (uint32_t)(mlpl::rm_w_bytes(kw, l) / 16);
             p.items[l] = p.first[l] + (uint32_t)(mlpl::rm_b_bytes(kw, l) / 16);
         }
+    }
+}
+
+void fill_pack_args_layered(const int *widths, int l0, int count, PackArgs &p)
+{
+    p.layout = kPacked;
+    p.natural = 1;
+    for (int i = 0; i < count; ++i) {
+        const int win = widths[l0 + i], wout = widths[l0 + i + 1];
+        const size_t off = layered_layer_offset(widths, l0 + i);
+        p.win[i] = win;
+        p.wout[i] = wout;
+        p.mt[i] = layered_kout(wout) / 32;
+        p.kb[i] = layered_kin(win) / 16;
+        p.a_off[i] = (uint32_t)off;
+        p.b_off[i] = (uint32_t)(off + layered_a_bytes(win, wout));
+        p.first[i] = (uint32_t)(p.mt[i] * p.kb[i] * 64);
+        p.items[i] = p.first[i] + (uint32_t)(p.mt[i] * 2);
     }
 }
 

@@ -41,9 +41,13 @@ def _err(fn, *args):
 
 def test_shape_validation():
     assert _err(B.mlp_packed_size, [], 1) == B.MLP_ERR_INVALID_ARGUMENT            # n_layers 0 (one width)
-    assert _err(B.mlp_packed_size, [4] * 10, 1) == B.MLP_ERR_INVALID_ARGUMENT      # 9 layers
+    assert _err(B.mlp_packed_size, [4] * 66, 1) == B.MLP_ERR_INVALID_ARGUMENT      # 65 layers
     assert _err(B.mlp_packed_size, [4, 0, 4], 1) == B.MLP_ERR_INVALID_ARGUMENT
-    assert _err(B.mlp_packed_size, [4, 129, 4], 1) == B.MLP_ERR_INVALID_ARGUMENT
+    assert _err(B.mlp_packed_size, [4, 4097, 4], 1) == B.MLP_ERR_INVALID_ARGUMENT
+    # beyond the fused limits: the layer-by-layer path (packed layout only)
+    assert B.mlp_packed_size([4, 129, 4], 1) > 0
+    assert B.mlp_packed_size([4] * 10, 1) > 0
+    assert _err(B.mlp_packed_size, [4, 129, 4], B.MLP_LAYOUT_ROW_MAJOR) == B.MLP_ERR_UNSUPPORTED
     assert _err(B.mlp_packed_size, [4, 4], 7) == B.MLP_ERR_INVALID_ARGUMENT        # unknown layout
     assert "widths[1]" in B.mlp_last_error() or "layout" in B.mlp_last_error()
     # row-major is compiled only for the dedicated shapes
@@ -115,6 +119,54 @@ def test_plan_widths():
     assert B.mlp_plan_widths(workloads.get("page").widths) == [32] + [64] * 7 + [32]
     assert B.mlp_plan_widths(workloads.get("hetero").widths) == [32, 64, 64, 64, 128, 64, 64, 32, 32]
     assert B.mlp_plan_widths([2, 2, 1]) == [128, 128, 128]  # generic kernel, zero-padded
+    assert B.mlp_plan_widths([100, 300, 129, 7]) == [128, 384, 256, 128]  # layer by layer
+    assert B.mlp_plan_widths([16] * 10) == [32] + [128] * 9
+
+
+# ---- an independent reading of the layer-by-layer image ------------------------------------------
+#
+# Per layer: A fragments [MT][KB][lane][8] with MT = ceil(w_out / 128) * 4, KB = ceil(w_in / 32) * 2,
+# lane = 32 g + m holding row 32 mt + m and input features 16 kb + 8 g + j (natural order); then the
+# bias tiles [MT][g][16] FP32 with entry (mt, g, j) = b[32 mt + 8 (j // 4) + 4 g + j % 4].
+
+def _unpack_layered(image, widths):
+    off = 0
+    Ws, bs = [], []
+    for l in range(len(widths) - 1):
+        MT = -(-widths[l + 1] // 128) * 4
+        KB = -(-widths[l] // 32) * 2
+        A = image[off:off + MT * KB * 1024].view(np.uint16).reshape(MT, KB, 2, 32, 8)
+        off += MT * KB * 1024
+        bias = image[off:off + MT * 128].view(np.float32).reshape(MT, 2, 16)
+        off += MT * 128
+        full = np.zeros((MT * 32, KB * 16), np.uint16)
+        bfull = np.zeros(MT * 32, np.float32)
+        for mt in range(MT):
+            for g in range(2):
+                for j in range(16):
+                    bfull[32 * mt + 8 * (j // 4) + 4 * g + j % 4] = bias[mt, g, j]
+                for kb in range(KB):
+                    full[32 * mt:32 * mt + 32, 16 * kb + 8 * g:16 * kb + 8 * g + 8] = A[mt, kb, g]
+        Ws.append(full)
+        bs.append(bfull)
+    assert off == image.size
+    return Ws, bs
+
+
+@pytest.mark.parametrize("widths", [(100, 300, 129, 7), (16,) * 10, (256, 32, 200)])
+def test_layered_image_layout(widths):
+    Ws, bs = workloads.init_weights(widths, seed=5)
+    image = B.mlp_pack_host(Ws, bs, B.MLP_LAYOUT_PACKED)
+    assert image.size == B.mlp_packed_size(widths)
+    UW, Ub = _unpack_layered(image, widths)
+    for l in range(len(widths) - 1):
+        wout, win = Ws[l].shape
+        assert np.array_equal(UW[l][:wout, :win], Ws[l].view(np.uint16)), l
+        pad = UW[l].copy()
+        pad[:wout, :win] = 0
+        assert not pad.any(), "padding must be zero"
+        assert np.array_equal(Ub[l][:wout], bs[l].astype(np.float32)), l
+        assert not Ub[l][wout:].any()
 
 
 # ---- an independent reading of the packed layout ---------------------------------------------
