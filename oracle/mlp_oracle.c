@@ -177,3 +177,138 @@ void oracle_leaky_f16_array(int64_t n, const uint16_t *in, uint16_t *out)
     for (int64_t i = 0; i < n; ++i)
         out[i] = oracle_leaky_f16(in[i]);
 }
+
+/* ---------------------------------------------------------------------------------------- */
+/* the FP8 variant                                                                          */
+/* ---------------------------------------------------------------------------------------- */
+/*
+ * A lower-precision form of the same network (the survey's "next" step after the FP16 path; the
+ * pages point to lower precisions and to block-scaled formats that carry one power-of-two scale per
+ * block of elements).  Readings taken here, listed with the design notes:
+ *   - format: OCP FP8 E4M3 (1 sign bit, 4 exponent bits with bias 7, 3 fraction bits; subnormals
+ *     f * 2^-9; the code S.1111.111 is NaN, there is no infinity, the largest finite value is 448);
+ *   - conversion to E4M3: round to nearest, ties to even; a magnitude above 464 (the midpoint
+ *     between 448 and the next, unrepresentable step 480) becomes NaN -- no saturation;
+ *   - weights: each output row r of W_l gets the power of two 2^E_r with the smallest E_r such that
+ *     max_k |W_l[r][k]| <= 448 * 2^E_r (E_r = 0 for an all-zero row); q = E4M3(W / 2^E_r);
+ *   - activations: each layer's input h (binary16) is stored as x8 = E4M3(16 * h);
+ *   - layer: acc = f32(b[r]) + sum_k (q[r][k] * 2^E_r) * (x8[k] * 2^-4) in binary32, k ascending
+ *     (every product is exact in binary32), then RNE16 and the binary16 leaky ReLU as in the FP16
+ *     network, none after the last layer.
+ */
+
+/* Value of an E4M3 code. */
+float oracle_e4m3_to_f32(uint8_t c)
+{
+    const int sign = (c >> 7) & 1, e = (c >> 3) & 0xf, f = c & 7;
+    float mag;
+    if (e == 0xf && f == 7)
+        mag = NAN;
+    else if (e == 0)
+        mag = ldexpf((float)f, -9); /* f/8 * 2^-6 */
+    else
+        mag = ldexpf((float)(8 + f), e - 10); /* (1 + f/8) * 2^(e-7) */
+    return sign ? -mag : mag;
+}
+
+/* binary32 -> E4M3, nearest even, NaN above 464 (same scheme as the binary16 encoder: the
+ * magnitude over the binade's spacing is exact in double and rint() rounds it, ties to even). */
+uint8_t oracle_f32_to_e4m3(float x)
+{
+    const uint8_t sign = signbit(x) ? 0x80 : 0;
+    if (isnan(x))
+        return sign | 0x7f;
+    const double a = fabs((double)x);
+    if (a > 464.0)
+        return sign | 0x7f;
+    if (a < ldexp(1.0, -6)) {
+        const double r = rint(a / ldexp(1.0, -9)); /* 0 .. 8; 8 encodes 2^-6 (exponent field 1) */
+        return sign | (uint8_t)r;
+    }
+    int e2;
+    frexp(a, &e2);
+    const int e = e2 - 1;                        /* a in [2^e, 2^(e+1)), e in -6 .. 8 */
+    const double r = rint(a / ldexp(1.0, e - 3)); /* 8 .. 16 */
+    return sign | (uint8_t)(((e + 7) << 3) + (int)(r - 8.0));
+}
+
+/* E_r of a weight row of binary16 values: the smallest E with max |w| <= 448 * 2^E. */
+int oracle_fp8_row_exponent(const uint16_t *row, int n)
+{
+    double amax = 0.0;
+    for (int k = 0; k < n; ++k) {
+        const double a = fabs((double)oracle_f16_to_f32(row[k]));
+        if (a > amax)
+            amax = a;
+    }
+    if (amax == 0.0)
+        return 0;
+    int E = -60;
+    while (amax > ldexp(448.0, E))
+        ++E;
+    return E;
+}
+
+/* The FP8 network on rows of x (binary16 bits), as described above. */
+int oracle_mlp_forward_fp8(int n_layers, const int32_t *widths, const uint16_t *const *weights,
+                           const uint16_t *const *biases, int64_t rows, const uint16_t *x, uint16_t *y)
+{
+    if (n_layers < 1 || !widths || !weights || !biases || rows < 0 || (rows > 0 && (!x || !y)))
+        return ORACLE_BAD_ARG;
+    for (int l = 0; l <= n_layers; ++l)
+        if (widths[l] < 1 || widths[l] > ORACLE_MAX_WIDTH)
+            return ORACLE_BAD_ARG;
+    /* quantise every layer's weights once */
+    float *wq[64];
+    if (n_layers > 64)
+        return ORACLE_BAD_ARG;
+    for (int l = 0; l < n_layers; ++l) {
+        const int win = widths[l], wout = widths[l + 1];
+        wq[l] = (float *)malloc(sizeof(float) * (size_t)win * wout);
+        for (int r = 0; r < wout; ++r) {
+            const uint16_t *row = weights[l] + (size_t)r * win;
+            const int E = oracle_fp8_row_exponent(row, win);
+            for (int k = 0; k < win; ++k) {
+                const uint8_t q = oracle_f32_to_e4m3(ldexpf(oracle_f16_to_f32(row[k]), -E));
+                wq[l][(size_t)r * win + k] = ldexpf(oracle_e4m3_to_f32(q), E);
+            }
+        }
+    }
+    uint16_t h[ORACLE_MAX_WIDTH], next[ORACLE_MAX_WIDTH];
+    float xq[ORACLE_MAX_WIDTH];
+    for (int64_t r = 0; r < rows; ++r) {
+        memcpy(h, x + r * widths[0], sizeof(uint16_t) * widths[0]);
+        for (int l = 0; l < n_layers; ++l) {
+            const int win = widths[l], wout = widths[l + 1];
+            for (int k = 0; k < win; ++k)
+                xq[k] = ldexpf(oracle_e4m3_to_f32(oracle_f32_to_e4m3(16.0f * oracle_f16_to_f32(h[k]))), -4);
+            for (int j = 0; j < wout; ++j) {
+                float acc = oracle_f16_to_f32(biases[l][j]);
+                for (int k = 0; k < win; ++k)
+                    acc = acc + wq[l][(size_t)j * win + k] * xq[k];
+                uint16_t v = oracle_f32_to_f16(acc);
+                if (l + 1 < n_layers)
+                    v = oracle_leaky_f16(v);
+                next[j] = v;
+            }
+            memcpy(h, next, sizeof(uint16_t) * wout);
+        }
+        memcpy(y + r * widths[n_layers], h, sizeof(uint16_t) * widths[n_layers]);
+    }
+    for (int l = 0; l < n_layers; ++l)
+        free(wq[l]);
+    return ORACLE_OK;
+}
+
+/* Array forms of the E4M3 codec (for the exhaustive checks). */
+void oracle_f32_to_e4m3_array(int64_t n, const float *x, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_e4m3(x[i]);
+}
+
+void oracle_e4m3_to_f32_array(int64_t n, const uint8_t *c, float *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3_to_f32(c[i]);
+}

@@ -49,9 +49,14 @@ def _bind(path: Path) -> ctypes.CDLL:
     L.oracle_mlp_forward.restype = ctypes.c_int
     L.oracle_mlp_forward_rows.argtypes = [ctypes.c_int, p, p, p, p, ctypes.c_int64, p, p]
     L.oracle_mlp_forward_rows.restype = ctypes.c_int
-    for name in ("oracle_f32_to_f16_array", "oracle_f16_to_f32_array", "oracle_leaky_f16_array"):
+    for name in ("oracle_f32_to_f16_array", "oracle_f16_to_f32_array", "oracle_leaky_f16_array",
+                 "oracle_f32_to_e4m3_array", "oracle_e4m3_to_f32_array"):
         getattr(L, name).argtypes = [ctypes.c_int64, p, p]
         getattr(L, name).restype = None
+    L.oracle_fp8_row_exponent.argtypes = [p, ctypes.c_int]
+    L.oracle_fp8_row_exponent.restype = ctypes.c_int
+    L.oracle_mlp_forward_fp8.argtypes = [ctypes.c_int, p, p, p, ctypes.c_int64, p, p]
+    L.oracle_mlp_forward_fp8.restype = ctypes.c_int
     return L
 
 
@@ -111,7 +116,30 @@ class Oracle:
         self.L.oracle_leaky_f16_array(h.size, _ptr(h), _ptr(out))
         return out
 
+    # ---- FP8 E4M3 codec (the FP8 variant) --------------------------------------------------
+
+    def f32_to_e4m3(self, x) -> np.ndarray:
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, dtype=np.uint8)
+        self.L.oracle_f32_to_e4m3_array(x.size, _ptr(x), _ptr(out))
+        return out
+
+    def e4m3_to_f32(self, c) -> np.ndarray:
+        c = np.ascontiguousarray(c, dtype=np.uint8)
+        out = np.empty(c.shape, dtype=np.float32)
+        self.L.oracle_e4m3_to_f32_array(c.size, _ptr(c), _ptr(out))
+        return out
+
+    def fp8_row_exponent(self, row_bits) -> int:
+        r = _as_bits(row_bits).ravel()
+        return int(self.L.oracle_fp8_row_exponent(_ptr(r), r.size))
+
     # ---- network ---------------------------------------------------------------------------
+
+    def mlp_forward_fp8(self, weights, biases, x, threads: int = 1) -> np.ndarray:
+        """The FP8 variant of the network (E4M3 weights with a power-of-two scale per output row,
+        E4M3 activations scaled by 16); same conventions as ``mlp_forward``."""
+        return self._forward(self.L.oracle_mlp_forward_fp8, weights, biases, x, threads)
 
     def mlp_forward(self, weights, biases, x, threads: int = 1) -> np.ndarray:
         """Evaluate every row of ``x`` ([rows, widths[0]], fp16 or its uint16 bits).
@@ -135,6 +163,25 @@ class Oracle:
                                           ctypes.c_void_p(y.ctypes.data + lo * y.strides[0]))
                 if rc != 0:
                     raise RuntimeError("oracle_mlp_forward failed (%d)" % rc)
+
+        _sharded(run, rows, threads)
+        return y
+
+    def _forward(self, fn, weights, biases, x, threads):
+        net = _Net(weights, biases)
+        x = _as_bits(x)
+        if x.ndim != 2 or x.shape[1] != net.widths[0]:
+            raise ValueError("x must be [rows, %d]" % net.widths[0])
+        rows = x.shape[0]
+        y = np.empty((rows, int(net.widths[-1])), dtype=np.uint16)
+
+        def run(lo, hi):
+            if hi > lo:
+                rc = fn(net.n_layers, _ptr(net.widths), net.wp, net.bp, hi - lo,
+                        ctypes.c_void_p(x.ctypes.data + lo * x.strides[0]),
+                        ctypes.c_void_p(y.ctypes.data + lo * y.strides[0]))
+                if rc != 0:
+                    raise RuntimeError("oracle forward failed (%d)" % rc)
 
         _sharded(run, rows, threads)
         return y
@@ -198,6 +245,10 @@ def mlp_forward(weights, biases, x, threads: int = 1):
 
 def mlp_forward_rows(weights, biases, x, row_index, threads: int = 1):
     return default().mlp_forward_rows(weights, biases, x, row_index, threads)
+
+
+def mlp_forward_fp8(weights, biases, x, threads: int = 1):
+    return default().mlp_forward_fp8(weights, biases, x, threads)
 
 
 def _sharded(fn, n: int, threads: int) -> None:

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import test_oracle_codec as codec
+import test_oracle_fp8 as fp8
 import test_oracle_pins as pins
 from oracle import oracle as oracle_pkg
 
@@ -34,6 +35,36 @@ MUTANTS = {
 }
 
 
+# Planted mistakes in the FP8 variant; each must fail one of the FP8 pins.
+FP8_MUTANTS = {
+    "fp8_activation_not_scaled": ("oracle_f32_to_e4m3(16.0f * oracle_f16_to_f32(h[k]))",
+                                  "oracle_f32_to_e4m3(oracle_f16_to_f32(h[k]))"),
+    "fp8_activation_not_quantised": (
+        "xq[k] = ldexpf(oracle_e4m3_to_f32(oracle_f32_to_e4m3(16.0f * oracle_f16_to_f32(h[k]))), -4);",
+        "xq[k] = oracle_f16_to_f32(h[k]);"),
+    "fp8_weight_not_quantised": ("wq[l][(size_t)r * win + k] = ldexpf(oracle_e4m3_to_f32(q), E);",
+                                 "wq[l][(size_t)r * win + k] = oracle_f16_to_f32(row[k]) + 0.0f * q;"),
+    "fp8_row_exponent_mx_floor": ("while (amax > ldexp(448.0, E))", "while (amax >= ldexp(512.0, E))"),
+    "fp8_truncating_encoder": ("const double r = rint(a / ldexp(1.0, e - 3));",
+                               "const double r = trunc(a / ldexp(1.0, e - 3));"),
+    "fp8_saturating_encoder": ("if (a > 464.0)\n        return sign | 0x7f;", "if (a > 464.0)\n        return sign | 0x7e;"),
+    "fp8_subnormal_scale": ("mag = ldexpf((float)f, -9);", "mag = ldexpf((float)f, -10);"),
+}
+
+
+def _quick_pins_fp8(o):
+    yield lambda: fp8.test_encoder_matches_torch_on_binary16_values(o)
+    yield lambda: fp8.test_decoder_matches_torch(o)
+    yield lambda: fp8.test_row_exponent_keeps_the_row_in_range(o)
+    import json
+
+    for case in json.loads(fp8.GOLDEN.read_text())["cases"]:
+        yield lambda case=case: fp8.test_hand_worked_examples(o, case)
+    for seed in range(3):
+        yield lambda seed=seed: fp8.test_integer_exact_nets_match_int64_brute_force(o, seed)
+    yield lambda: fp8.test_fp8_network_is_close_to_the_fp16_network(o, "page")
+
+
 def _quick_pins(o):
     yield lambda: pins.test_hand_worked_two_layer_net(o)
     yield lambda: pins.test_sign_alternating_diagonal_net(o)
@@ -54,6 +85,8 @@ def _quick_pins(o):
 def test_real_oracle_passes_the_quick_pins(oracle_mod):
     for pin in _quick_pins(oracle_mod):
         pin()
+    for pin in _quick_pins_fp8(oracle_mod):
+        pin()
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -73,3 +106,23 @@ def test_mutant_is_caught(tmp_path, name):
             caught.append(type(e).__name__)
             break
     assert caught, "mutant %r passed every pin" % name
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(tmp_path, name):
+    old, new = FP8_MUTANTS[name]
+    old, new = old.replace("\\n", "\n"), new.replace("\\n", "\n")
+    src = (oracle_pkg._SRC).read_text()
+    assert src.count(old) == 1, "mutation anchor not found exactly once: " + old
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle_pkg.build(force=True, src=mutant_src, out=tmp_path / "libmutant.so")
+    o = oracle_pkg.Oracle(lib)
+    caught = []
+    for pin in _quick_pins_fp8(o):
+        try:
+            pin()
+        except (AssertionError, ValueError, RuntimeError) as e:
+            caught.append(type(e).__name__)
+            break
+    assert caught, "mutant %r passed every FP8 pin" % name
