@@ -187,6 +187,15 @@ def measure_workloads(torch, B, workloads, skip: str) -> dict:
         if name != skip:
             rounds = [variant_medians(torch, B, wl, Ws, bs, x, y, (0, 1) if r % 2 == 0 else (1, 0)) for r in range(3)]
             entry["variants"] = summarise_variants(rounds, wl)
+        # the FP8 variant (E4M3 weights and activations, FP32 accumulation): same timing
+        B.mlp_pack_weights(Ws, bs, B.MLP_LAYOUT_PACKED_FP8, sh)
+        for _ in range(3):
+            f()
+        ms8 = statistics.median(time_dispatches(torch, f, 20))
+        entry["fp8"] = {"median_ms": round(ms8, 6), "m_evals_per_s": round(throughput_m_evals(wl.batch, ms8), 1),
+                        "speedup_vs_fp16": round(ms / ms8, 3),
+                        "equiv_tflops": round(wl.flops_per_eval * wl.batch / (ms8 * 1e-3) / 1e12, 1),
+                        "kernel": B.mlp_kernel_name(B.MLP_ACT_VECTOR)}
         res[name] = entry
         del x, y
         torch.cuda.empty_cache()

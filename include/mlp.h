@@ -43,7 +43,12 @@ typedef enum mlp_status {
 /* Weight layouts ("Row-major versus InferencingOptimal weights"). */
 enum {
     MLP_LAYOUT_ROW_MAJOR = 0, /* the canonical FP16 row-major matrices, read as they are          */
-    MLP_LAYOUT_PACKED = 1     /* converted once into MFMA-fragment order (the default)            */
+    MLP_LAYOUT_PACKED = 1,    /* converted once into MFMA-fragment order (the default)            */
+    MLP_LAYOUT_PACKED_FP8 = 2 /* the FP8 variant: weights converted once to OCP E4M3 with a       */
+                              /* power-of-two scale per output row (the smallest keeping the row  */
+                              /* within 448), each layer's input stored as E4M3(16 h), FP32       */
+                              /* accumulation, then FP16 rounding and leaky ReLU as in FP16; for  */
+                              /* the dedicated shapes, vector activation, host packing only       */
 };
 
 /* Activation forms ("Bad versus good activation"); both compute the same function, bit for bit. */

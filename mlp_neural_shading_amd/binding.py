@@ -24,6 +24,7 @@ MLP_ERR_OUT_OF_MEMORY = -4
 MLP_ERR_HIP = -5
 MLP_LAYOUT_ROW_MAJOR = 0
 MLP_LAYOUT_PACKED = 1
+MLP_LAYOUT_PACKED_FP8 = 2
 MLP_ACT_VECTOR = 0
 MLP_ACT_SCALARISED = 1
 MLP_MAX_LAYERS = 64

@@ -26,7 +26,7 @@ COMMON = [
     # wave-aggregating rewrite of atomics would consume the result at once and stall the wave
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
-SOURCES = ["mlp_kernels.hip", "mlp_layered.hip", "mlp_pack_device.hip", "mlp_api.cpp", "mlp_pack.cpp"]
+SOURCES = ["mlp_kernels.hip", "mlp_kernels_fp8.hip", "mlp_layered.hip", "mlp_pack_device.hip", "mlp_api.cpp", "mlp_pack.cpp"]
 CEILING_SOURCE = "mlp_ceiling.hip"
 CEILING_LIB = PKG / "libmlp_ceiling.so"
 

@@ -116,7 +116,7 @@ int check_shape(int n_layers, const int32_t *widths)
 
 int check_layout(int layout)
 {
-    if (layout != MLP_LAYOUT_ROW_MAJOR && layout != MLP_LAYOUT_PACKED)
+    if (layout != MLP_LAYOUT_ROW_MAJOR && layout != MLP_LAYOUT_PACKED && layout != MLP_LAYOUT_PACKED_FP8)
         return fail(MLP_ERR_INVALID_ARGUMENT, "unknown layout %d", layout);
     return MLP_OK;
 }
@@ -135,6 +135,11 @@ const KernelEntry *select(int n_layers, const int32_t *widths, int layout, int a
 {
     int count = 0;
     const KernelEntry *all = mlpk::registry(&count);
+    if (layout == MLP_LAYOUT_PACKED_FP8) {  // dedicated shapes only
+        all = mlpk::registry_fp8(&count);
+        if (act != MLP_ACT_VECTOR)
+            return nullptr;
+    }
     for (int i = 0; i < count; ++i) {
         const KernelEntry &e = all[i];
         if (e.generic || e.n_layers != n_layers || e.layout != layout || e.act != act)
@@ -167,8 +172,9 @@ int plan(int n_layers, const int32_t *widths, int layout, const KernelEntry **ou
     if (!e && layout == MLP_LAYOUT_PACKED)
         e = &kLayered;  // wider or deeper than the fused kernels
     if (!e)
-        return fail(MLP_ERR_UNSUPPORTED, "no kernel serves this shape with the %s layout (row-major is "
-                    "compiled for the dedicated shapes only)", layout == MLP_LAYOUT_PACKED ? "packed" : "row-major");
+        return fail(MLP_ERR_UNSUPPORTED, "no kernel serves this shape with the %s layout (row-major and FP8 are "
+                    "compiled for the dedicated shapes only)",
+                    layout == MLP_LAYOUT_PACKED ? "packed" : layout == MLP_LAYOUT_ROW_MAJOR ? "row-major" : "FP8");
     *out = e;
     return MLP_OK;
 }

@@ -95,4 +95,39 @@ constexpr size_t rml_w_off(const int *w, int l)
 constexpr size_t rml_b_off(const int *w, int l) { return rml_w_off(w, l) + rml_w_bytes(w, l); }
 constexpr size_t rml_bytes(const int *w, int L) { return rml_w_off(w, L); }
 
+// ---- FP8 image (v_mfma_f32_32x32x64_f8f6f4, OCP E4M3 operands) ------------------------------
+//
+// The FP8 MFMA takes 64 input features per block: lane (g, m) of the A operand holds 32 bytes, slots
+// j = 0..31 of group g for row m, and pairs slot (g, j) with the same slot of the B operand (lane
+// (g, n), sample n); the 32x32 FP32 result has the same lane layout as the FP16 MFMA's.  Slots:
+//   layer 0 (reads the caller's rows): slot (kb, g, j) = feature 64 kb + 32 g + j;
+//   layer l >= 1: output tiles 2 kb and 2 kb + 1 of the previous layer fill block kb, the first in
+//     slots 0..15 and the second in 16..31, each as its accumulator elements in order:
+//     slot (kb, g, j) = feature 32 (2 kb + j / 16) + 8 ((j % 16) / 4) + 4 g + j % 4.
+// Per layer: A fragments [mt][kb][lane][32 bytes] (2 KB each), then the row scales
+// [ceil(MT / 4)][lane][4 bytes] (byte i of lane (g, m)'s word: the E8M0 code of row
+// 32 (4 q + i) + m, selected by the MFMA's op_sel), then FP32 bias tiles as in the FP16 image.
+constexpr int kF8FragBytes = 64 * 32;
+constexpr int f8_k_blocks(const int *w, int l) { return (w[l] + 63) / 64; }
+constexpr int f8_slot_feature(int l, int kb, int g, int j)
+{
+    return l == 0 ? 64 * kb + 32 * g + j : 32 * (2 * kb + j / 16) + 8 * ((j % 16) / 4) + 4 * g + j % 4;
+}
+constexpr size_t f8_a_bytes(const int *w, int l) { return (size_t)m_tiles(w, l) * f8_k_blocks(w, l) * kF8FragBytes; }
+constexpr size_t f8_s_bytes(const int *w, int l) { return (size_t)((m_tiles(w, l) + 3) / 4) * 256; }
+constexpr size_t f8_layer_bytes(const int *w, int l)
+{
+    return f8_a_bytes(w, l) + f8_s_bytes(w, l) + (size_t)m_tiles(w, l) * kBiasTileBytes;
+}
+constexpr size_t f8_a_off(const int *w, int l)
+{
+    size_t o = 0;
+    for (int i = 0; i < l; ++i)
+        o += f8_layer_bytes(w, i);
+    return o;
+}
+constexpr size_t f8_s_off(const int *w, int l) { return f8_a_off(w, l) + f8_a_bytes(w, l); }
+constexpr size_t f8_b_off(const int *w, int l) { return f8_s_off(w, l) + f8_s_bytes(w, l); }
+constexpr size_t f8_bytes(const int *w, int L) { return f8_a_off(w, L); }
+
 }  // namespace mlpl

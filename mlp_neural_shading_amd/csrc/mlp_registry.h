@@ -7,7 +7,7 @@
 
 namespace mlpk {
 
-enum Layout { kRowMajor = 0, kPacked = 1 };
+enum Layout { kRowMajor = 0, kPacked = 1, kPackedFp8 = 2 };
 enum Act { kVector = 0, kScalarised = 1 };
 
 // Everything one launch needs; passed by value as the kernel argument.
@@ -34,7 +34,8 @@ struct KernelEntry {
     const void *func;   // kernel symbol, for occupancy queries
 };
 
-// All compiled instances.
+// All compiled instances: the FP16 kernels and the FP8 ones.
 const KernelEntry *registry(int *count);
+const KernelEntry *registry_fp8(int *count);
 
 }  // namespace mlpk

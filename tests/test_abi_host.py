@@ -244,3 +244,67 @@ def test_row_major_image_is_verbatim(name):
         assert np.array_equal(image[off:off + n].view(np.uint16), b.view(np.uint16))
         off += -(-n // 16) * 16
     assert off == image.size
+
+
+# ---- the FP8 image, read independently (E4M3 values via PyTorch's float8_e4m3fn) ------------------
+#
+# Per layer: A fragments [MT][KB][lane][32 bytes] (KB = ceil(w_in / 64)), lane = 32 g + m holding row
+# 32 mt + m; slot j of block kb holds feature 64 kb + 32 g + j for layer 0 and
+# 32 (2 kb + j // 16) + 8 ((j % 16) // 4) + 4 g + j % 4 after; then scale words
+# [ceil(MT / 4)][lane][4 bytes] (byte i: E8M0 code of row 32 (4 q + i) + m); then FP32 bias tiles.
+
+def _torch_e4m3_codes(x):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_fp8_image_layout(name):
+    widths = workloads.WORKLOADS[name].widths
+    Ws, bs = workloads.init_weights(widths)
+    image = B.mlp_pack_host(Ws, bs, B.MLP_LAYOUT_PACKED_FP8)
+    assert image.size == B.mlp_packed_size(widths, B.MLP_LAYOUT_PACKED_FP8)
+    off = 0
+    for l in range(len(widths) - 1):
+        win, wout = widths[l], widths[l + 1]
+        MT, KB = -(-wout // 32), -(-win // 64)
+        A = image[off:off + MT * KB * 2048].reshape(MT, KB, 2, 32, 32)
+        off += MT * KB * 2048
+        nq = -(-MT // 4)
+        S = image[off:off + nq * 256].reshape(nq, 2, 32, 4)
+        off += nq * 256
+        bias = image[off:off + MT * 128].view(np.float32).reshape(MT, 2, 16)
+        off += MT * 128
+        W = Ws[l].astype(np.float64)
+        for mt in range(MT):
+            for m in range(32):
+                r = 32 * mt + m
+                code = int(S[mt // 4, 0, m, mt % 4])
+                assert code == int(S[mt // 4, 1, m, mt % 4])  # both lane groups carry the row's scale
+                if r >= wout:
+                    assert code == 127 and not A[mt, :, :, m].any()
+                    continue
+                E = code - 127
+                amax = np.abs(W[r]).max()
+                assert amax == 0 or 224 < amax / 2.0 ** E <= 448, (l, r, E, amax)
+                # every weight is the E4M3 code nearest to w / 2^E (PyTorch's float8_e4m3fn conversion)
+                want = _torch_e4m3_codes((W[r] / 2.0 ** E).astype(np.float32))
+                for kb in range(KB):
+                    for g in range(2):
+                        for j in range(32):
+                            f = 64 * kb + 32 * g + j if l == 0 else 32 * (2 * kb + j // 16) + 8 * ((j % 16) // 4) + 4 * g + j % 4
+                            got = int(A[mt, kb, g, m, j])
+                            assert got == (int(want[f]) if f < win else 0), (l, r, f)
+        for mt in range(MT):
+            for g in range(2):
+                for j in range(16):
+                    r = 32 * mt + 8 * (j // 4) + 4 * g + j % 4
+                    assert bias[mt, g, j] == (np.float32(bs[l][r]) if r < wout else 0.0)
+    assert off == image.size
+
+
+def test_fp8_is_for_the_dedicated_shapes():
+    assert B.mlp_packed_size(workloads.get("page").widths, B.MLP_LAYOUT_PACKED_FP8) > 0
+    assert _err(B.mlp_packed_size, [5, 7, 3], B.MLP_LAYOUT_PACKED_FP8) == B.MLP_ERR_UNSUPPORTED
+    assert _err(B.mlp_packed_size, [4, 4], 3) == B.MLP_ERR_INVALID_ARGUMENT
