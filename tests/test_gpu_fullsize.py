@@ -61,7 +61,9 @@ def test_page_workload_full(oracle_mod):
         assert torch.equal(y2, y), (layout, act)
 
 
-@pytest.mark.parametrize("name,n_random,edge", [("small", 0, 4096), ("hetero", 24576, 1024), ("wide", 6144, 512)])
+# small and hetero: every row (4,096 and 1,048,576); wide (4,194,304 rows of 107,008 MACs): the first
+# and last 65,536 rows and a seeded random sample.
+@pytest.mark.parametrize("name,n_random,edge", [("small", 0, 4096), ("hetero", 0, 524288), ("wide", 16384, 65536)])
 def test_full_size_sampled(oracle_mod, name, n_random, edge):
     import torch
 
@@ -75,8 +77,8 @@ def test_full_size_sampled(oracle_mod, name, n_random, edge):
 
 
 def test_streaming_workload_full(oracle_mod):
-    """67,108,864 distinct inputs (8 GiB in, 2 GiB out): sampled rows including those whose input
-    bytes straddle each 2 GiB boundary (64-bit addressing)."""
+    """67,108,864 distinct inputs (8 GiB in, 2 GiB out): the first and last 65,536 rows, the rows whose
+    input bytes straddle each 2 GiB boundary (64-bit addressing) and 262,144 seeded random rows."""
     import torch
 
     wl = workloads.get("stream")
@@ -88,7 +90,7 @@ def test_streaming_workload_full(oracle_mod):
     for k in (1, 2, 3):
         r = (k << 31) // row_bytes
         edges += list(range(r - 64, r + 64))
-    idx = _sample(wl, 16384, 512, extra=edges)
+    idx = _sample(wl, 262144, 65536, extra=edges)  # first / last 65,536 rows, 2 GiB edges, random rows
     ref = oracle_mod.mlp_forward_rows(Ws, bs, _rows_bits(x, idx), np.arange(idx.size), threads=host_threads())
     log("   ", compare(_rows_bits(y, idx), ref, what=wl.name), "rows checked", idx.size)
     del x, y
