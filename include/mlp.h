@@ -150,7 +150,9 @@ int mlp_debug_read_packed(void *host_dst, size_t bytes);
 /* Message for the last error on the calling thread ("" if none).  Valid until the next call. */
 const char *mlp_last_error(void);
 
-/* Free the current device image.  Idempotent; mlp_infer then returns MLP_ERR_NOT_PACKED. */
+/* Free the current device image and return the scratch memory the layer-by-layer path keeps cached
+ * (its stream-ordered frees complete first).  Idempotent; mlp_infer then returns MLP_ERR_NOT_PACKED.
+ * Not thread-safe with respect to mlp_pack_weights or an mlp_infer still being enqueued. */
 void mlp_release(void);
 
 #ifdef __cplusplus

@@ -72,9 +72,11 @@ constexpr int64_t kLayeredChunkRows = 65536;
 // no release threshold, so that the stream-ordered allocation of each call reuses memory.
 hipMemPool_t g_pool = nullptr;
 int g_pool_device = -1;
+std::mutex g_pool_mu;  // mlp_infer may be called from several threads at once
 
 int layered_pool(int device, hipMemPool_t *out)
 {
+    std::lock_guard<std::mutex> lock(g_pool_mu);
     if (!g_pool || g_pool_device != device) {
         hipMemPoolProps props = {};
         props.allocType = hipMemAllocationTypePinned;
@@ -536,6 +538,12 @@ const char *mlp_last_error(void) { return t_error.c_str(); }
 
 void mlp_release(void)
 {
+    {
+        // hand the layered path's cached scratch memory back (pending frees complete first)
+        std::lock_guard<std::mutex> lock(g_pool_mu);
+        if (g_pool)
+            (void)hipMemPoolTrimTo(g_pool, 0);
+    }
     if (g_net.packed)
         (void)hipFree(g_net.image);
     g_net = State();
