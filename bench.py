@@ -402,7 +402,10 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # After the GPU has been idle its first ~10 ms of work run ~10 % slower while the clock ramps up
+    # (measured: ~60 us per step for the first 200 page-net steps, 54.3 us afterwards); the default
+    # warm-up (~27 ms of the page net) covers that ramp.
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="page", help="workload name or alias (default: page)")
     ap.add_argument("--no-variants", action="store_true", help="skip the row-major / scalarised A/B")
     ap.add_argument("--layout", choices=("packed", "rowmajor"), default="packed",

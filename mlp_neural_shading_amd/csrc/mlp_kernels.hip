@@ -99,12 +99,24 @@ struct Net {
     static constexpr size_t lds_bytes(int layout) { return layout == kPacked ? mlpl::pk_bytes(w, L) : mlpl::rml_bytes(w, L); }
 };
 
-template <class N, int NT, int LAYOUT, int ACT, bool GENERIC, bool LDS_W, class Src>
+template <class N, int NT, int LAYOUT, int ACT, bool GENERIC, bool LDS_W, class Src, bool DEFER>
 struct Body {
     static constexpr int L = N::L;
     // Caller widths known at compile time (exact instances) allow vector loads and stores.
     static constexpr bool kVecIn = !GENERIC && N::w[0] % 8 == 0;
     static constexpr bool kVecOut = !GENERIC && N::w[L] % 4 == 0;
+    // The last layer's outputs are held in registers and stored at the top of the next tile, after
+    // that tile's inputs have been waited for: a store issued at the end of a tile would otherwise
+    // sit in front of the next tile's wait (the vector-memory counter counts stores too) and every
+    // tile would wait for its own store's round trip.  That wait only shows where fewer than three
+    // waves share a SIMD and the weights come from LDS (measured: -2.8 % on the net with a 128-wide
+    // layer; +0.4 % on the page net; +5 % on the net whose weights are read with buffer loads, where
+    // the held store would sit in front of every weight fetch instead), so the instance chooses.
+    static constexpr bool kDefer = DEFER && kVecOut && N::MT(L - 1) == 1;
+    static constexpr int kQ = (N::w[L] + 7) / 8;  // 8-output groups holding real outputs
+    struct Pending {
+        h4 v[NT][kQ];
+    };
 
     // ---- weight delivery ------------------------------------------------------------------
 
@@ -224,7 +236,7 @@ struct Body {
 
     template <int l>
     static __device__ __forceinline__ void layer(const Src &wb, const h8 (&Bin)[N::KB(l)][NT],
-                                                 const LaunchArgs &a, int64_t row0, int lane)
+                                                 const LaunchArgs &a, int64_t row0, int lane, Pending &pend)
     {
         constexpr int MT = N::MT(l), KB = N::KB(l);
         // Weights read through the caches: keep each layer's reads inside the layer, or the
@@ -259,7 +271,7 @@ struct Body {
                 }
             }
             epilogue<KBN>(MT - 1, prev, Bout);
-            layer<l + 1>(wb, Bout, a, row0, lane);
+            layer<l + 1>(wb, Bout, a, row0, lane, pend);
         } else {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -269,7 +281,10 @@ struct Body {
                     fetch<l>(wb, mt + 1, afn, biasn, lane);
                 f16x acc[NT];
                 mfmas<l>(af, Bin, bias, acc);
-                store_outputs(acc, mt, a, row0, lane, std::make_integer_sequence<int, NT>());
+                if constexpr (kDefer)
+                    hold_outputs(acc, pend);
+                else
+                    store_outputs(acc, mt, a, row0, lane, std::make_integer_sequence<int, NT>());
                 if (mt + 1 < MT) {
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
@@ -387,6 +402,37 @@ struct Body {
     {
         (store_tile<T>(acc, mt, a, row0, lane), ...);
     }
+
+    // Deferred form (one output tile, vector stores): convert now, store at the next tile's top.
+    static __device__ __forceinline__ void hold_outputs(const f16x (&acc)[NT], Pending &pend)
+    {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) {
+                const f4 part = {acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
+                pend.v[t][q] = __builtin_convertvector(part, h4);
+            }
+    }
+
+    static __device__ __forceinline__ void store_pending(const Pending &pend, const LaunchArgs &a, int64_t row0,
+                                                         int lane)
+    {
+        const int g = lane >> 5, n = lane & 31;
+        constexpr int wl = N::w[L];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int64_t row = row0 + 32 * t + n;
+            if (row < a.batch) {
+#pragma unroll
+                for (int q = 0; q < kQ; ++q) {
+                    const int c = 8 * q + 4 * g;
+                    if (c < wl)
+                        *(h4 *)((_Float16 *)a.y + row * wl + c) = pend.v[t][q];
+                }
+            }
+        }
+    }
 };
 
 // Copy the weight image into LDS with every load in flight before the first store (the copy is a
@@ -450,7 +496,7 @@ template <class N, int NT, int WAVES, int EU, bool LDS_W, int LAYOUT, int ACT, b
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(EU, EU))) mlp_fused(LaunchArgs a)
 {
     using Src = typename std::conditional<LDS_W, LdsSource, BufferSource>::type;
-    using B = Body<N, NT, LAYOUT, ACT, GENERIC, LDS_W, Src>;
+    using B = Body<N, NT, LAYOUT, ACT, GENERIC, LDS_W, Src, (EU < 3 && LDS_W)>;
     constexpr int bytes = (int)N::image_bytes(LAYOUT);
     constexpr int lbytes = (int)N::lds_bytes(LAYOUT);
     static_assert(bytes % 16 == 0, "image must be a multiple of 16 bytes");
@@ -491,6 +537,8 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
     int claimed = 0;
     if (lane == 0)
         claimed = atomicAdd(&next_tile, 1);
+    typename B::Pending pend;
+    int64_t held_row0 = -1;  // first row of the tile whose outputs are held in pend
     while (tile < hi) {
         // The weights are loop-invariant; without this barrier the compiler hoists every fragment
         // read out of the tile loop and the whole image (up to ~1 KB per lane) spills.  The barrier
@@ -507,15 +555,22 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
         } else {
             B::mask_inputs(B0, Bnext, a, tile * kRows, lane, std::make_integer_sequence<int, NT>());
         }
+        if constexpr (B::kDefer)
+            if (held_row0 >= 0)
+                B::store_pending(pend, a, held_row0, lane);
         if (next < hi)
             B::load_inputs(Bnext, a, next * kRows, lane, std::make_integer_sequence<int, NT>());
         const int64_t after = lo + __builtin_amdgcn_readfirstlane(claimed);  // claimed one tile ago
         if (lane == 0)
             claimed = atomicAdd(&next_tile, 1);
-        B::template layer<0>(src, B0, a, tile * kRows, lane);
+        B::template layer<0>(src, B0, a, tile * kRows, lane, pend);
+        held_row0 = tile * kRows;
         tile = next;
         next = after;
     }
+    if constexpr (B::kDefer)
+        if (held_row0 >= 0)
+            B::store_pending(pend, a, held_row0, lane);
 }
 
 template <class N, int NT, int WAVES, int EU, bool LDS_W, int LAYOUT, int ACT, bool GENERIC>
