@@ -437,15 +437,41 @@ struct Body {
 
 // Copy the weight image into LDS with every load in flight before the first store (the copy is a
 // handful of 16-byte loads per thread, so its cost is one round trip rather than one per load).
-// Written as an index-sequence expansion with constant indices: a loop-indexed staging array would
+// Written as index-sequence expansions with constant indices: a loop-indexed staging array would
 // be placed in LDS by the compiler.  Load addresses are clamped into the image; only in-range
 // chunks are stored.
+//
+// The loads and the stores are separate steps: the kernel issues the first tile's input loads in
+// between, behind the image loads, so the stores wait for the image (from L2) and not for the
+// inputs (every wave of the chip requests its first tile's inputs from HBM at the same moment).
+// The empty asm reads every loaded chunk before the first store: without it the compiler moves the
+// load of a chunk that only some threads store into the branch around that store, which turns the
+// copy into two round trips, the second behind the input loads.
+template <int C>
+struct Chunks {
+    uint4 v[C];
+};
+
+// An empty use of a loaded value: the load must have been issued (and waited for) before this point.
+__device__ __forceinline__ void loaded(const uint4 &v) { asm volatile("" ::"v"(v.x)); }
+
+// A 16-byte LDS store written component by component (a whole-struct copy kept the chunk array in
+// memory, which the compiler then placed in LDS).
+__device__ __forceinline__ void store16(uint8_t *dst, const uint4 &v) { *(uint4 *)dst = make_uint4(v.x, v.y, v.z, v.w); }
+
 template <int BYTES, int THREADS, int... K>
-__device__ __forceinline__ void stage_image(uint8_t *lds, const uint8_t *image, std::integer_sequence<int, K...>)
+__device__ __forceinline__ Chunks<sizeof...(K)> stage_load(const uint8_t *image, std::integer_sequence<int, K...>)
 {
     const int t16 = (int)threadIdx.x * 16;
-    const uint4 v[] = {*(const uint4 *)(image + (K * THREADS * 16 + t16 < BYTES ? K * THREADS * 16 + t16 : BYTES - 16))...};
-    ((K * THREADS * 16 + t16 < BYTES ? (void)(*(uint4 *)(lds + K * THREADS * 16 + t16) = v[K]) : (void)0), ...);
+    return {{*(const uint4 *)(image + (K * THREADS * 16 + t16 < BYTES ? K * THREADS * 16 + t16 : BYTES - 16))...}};
+}
+
+template <int BYTES, int THREADS, int... K>
+__device__ __forceinline__ void stage_store(uint8_t *lds, const Chunks<sizeof...(K)> &c, std::integer_sequence<int, K...>)
+{
+    const int t16 = (int)threadIdx.x * 16;
+    (loaded(c.v[K]), ...);
+    ((K * THREADS * 16 + t16 < BYTES ? store16(lds + K * THREADS * 16 + t16, c.v[K]) : (void)0), ...);
 }
 
 // LDS offset of the 16-byte chunk at byte offset g of a row-major image (all widths multiples of 8,
@@ -475,12 +501,13 @@ __device__ __forceinline__ void store_chunk8(uint8_t *dst, const uint4 &v)
 }
 
 template <class N, int BYTES, int THREADS, int... K>
-__device__ __forceinline__ void stage_rowmajor(uint8_t *lds, const uint8_t *image, std::integer_sequence<int, K...>)
+__device__ __forceinline__ void stage_store_rowmajor(uint8_t *lds, const Chunks<sizeof...(K)> &c,
+                                                     std::integer_sequence<int, K...>)
 {
     const int t16 = (int)threadIdx.x * 16;
-    const uint4 v[] = {*(const uint4 *)(image + (K * THREADS * 16 + t16 < BYTES ? K * THREADS * 16 + t16 : BYTES - 16))...};
+    (loaded(c.v[K]), ...);
     ((K * THREADS * 16 + t16 < BYTES
-          ? store_chunk8(lds + rowmajor_lds_offset<N>(K * THREADS * 16 + t16, std::make_integer_sequence<int, N::L>()), v[K])
+          ? store_chunk8(lds + rowmajor_lds_offset<N>(K * THREADS * 16 + t16, std::make_integer_sequence<int, N::L>()), c.v[K])
           : (void)0),
      ...);
 }
@@ -512,22 +539,23 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
     int64_t tile = lo + wave;
     int64_t next = lo + WAVES + wave;
 
-    // The first tile's inputs are requested before the weights are staged, so the two latencies
-    // overlap; every later tile's inputs are requested one tile ahead.
+    // The first tile's inputs are requested right behind the weight image's loads, so the two
+    // latencies overlap; every later tile's inputs are requested one tile ahead.
     constexpr int KB0 = N::KB(0);  // a constant expression, so the loops below fully unroll
     h8 Bnext[KB0][NT];
-    B::load_inputs(Bnext, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
-
     Src src;
     if constexpr (LDS_W) {
         __shared__ __attribute__((aligned(16))) uint8_t lds[lbytes];
         constexpr int kChunks = (bytes + WAVES * 64 * 16 - 1) / (WAVES * 64 * 16);
+        const auto chunks = stage_load<bytes, WAVES * 64>(a.image, std::make_integer_sequence<int, kChunks>());
+        B::load_inputs(Bnext, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
         if constexpr (LAYOUT == kPacked)
-            stage_image<bytes, WAVES * 64>(lds, a.image, std::make_integer_sequence<int, kChunks>());
+            stage_store<bytes, WAVES * 64>(lds, chunks, std::make_integer_sequence<int, kChunks>());
         else
-            stage_rowmajor<N, bytes, WAVES * 64>(lds, a.image, std::make_integer_sequence<int, kChunks>());
+            stage_store_rowmajor<N, bytes, WAVES * 64>(lds, chunks, std::make_integer_sequence<int, kChunks>());
         src.base = lds;
     } else {
+        B::load_inputs(Bnext, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
         src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.image, 0, bytes, kBufferRsrcWord3);
     }
     if (threadIdx.x == 0)
