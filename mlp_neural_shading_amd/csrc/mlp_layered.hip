@@ -60,7 +60,10 @@ __device__ __forceinline__ h8 load_x8(const LayerArgs &p, int64_t row, int c)
     return v;
 }
 
-__global__ __launch_bounds__(kThreads) void layer_gemm(LayerArgs p)
+// Four waves per SIMD (128 registers, no spills; four 36 KB workgroups per CU): more workgroups
+// in flight hide more of the operand loads' latency (-2.5 % on 1024-wide layers, -4 % on 256-wide
+// ones against three).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void layer_gemm(LayerArgs p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kABytes];
     __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kBBytes];
