@@ -303,13 +303,32 @@ struct Body {
     }
 };
 
-// Copy the image into LDS with every load in flight before the first store.
+// Copy the image into LDS with every load in flight before the first store, in two steps so that
+// the first tile's input loads can be issued in between: the stores then wait for the image (from
+// L2), not for the inputs (from HBM, requested by every wave of the chip at once).  The empty asm
+// reads every loaded chunk before the first store, so the compiler cannot move the load of a
+// partly used chunk into the branch around its store (a second round trip).
+template <int C>
+struct Chunks {
+    uint4 v[C];
+};
+
+__device__ __forceinline__ void loaded(const uint4 &v) { asm volatile("" ::"v"(v.x)); }
+__device__ __forceinline__ void store16(uint8_t *dst, const uint4 &v) { *(uint4 *)dst = make_uint4(v.x, v.y, v.z, v.w); }
+
 template <int BYTES, int THREADS, int... K>
-__device__ __forceinline__ void stage(uint8_t *lds, const uint8_t *image, std::integer_sequence<int, K...>)
+__device__ __forceinline__ Chunks<sizeof...(K)> stage_load(const uint8_t *image, std::integer_sequence<int, K...>)
 {
     const int t16 = (int)threadIdx.x * 16;
-    const uint4 v[] = {*(const uint4 *)(image + (K * THREADS * 16 + t16 < BYTES ? K * THREADS * 16 + t16 : BYTES - 16))...};
-    ((K * THREADS * 16 + t16 < BYTES ? (void)(*(uint4 *)(lds + K * THREADS * 16 + t16) = v[K]) : (void)0), ...);
+    return {{*(const uint4 *)(image + (K * THREADS * 16 + t16 < BYTES ? K * THREADS * 16 + t16 : BYTES - 16))...}};
+}
+
+template <int BYTES, int THREADS, int... K>
+__device__ __forceinline__ void stage_store(uint8_t *lds, const Chunks<sizeof...(K)> &c, std::integer_sequence<int, K...>)
+{
+    const int t16 = (int)threadIdx.x * 16;
+    (loaded(c.v[K]), ...);
+    ((K * THREADS * 16 + t16 < BYTES ? store16(lds + K * THREADS * 16 + t16, c.v[K]) : (void)0), ...);
 }
 
 // Scheduling as in the FP16 kernel: workgroup b owns tiles [lo, hi) of an even split; its waves take
@@ -333,9 +352,10 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
     int64_t next = lo + WAVES + wave;
 
     h8 Rnext[KB0][NT][4];
-    B::load_inputs(Rnext, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
     constexpr int kChunks = (bytes + WAVES * 64 * 16 - 1) / (WAVES * 64 * 16);
-    stage<bytes, WAVES * 64>(lds, a.image, std::make_integer_sequence<int, kChunks>());
+    const auto chunks = stage_load<bytes, WAVES * 64>(a.image, std::make_integer_sequence<int, kChunks>());
+    B::load_inputs(Rnext, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
+    stage_store<bytes, WAVES * 64>(lds, chunks, std::make_integer_sequence<int, kChunks>());
     if (threadIdx.x == 0)
         next_tile = 2 * WAVES;
     __syncthreads();
