@@ -358,6 +358,16 @@ def measure_ceiling(torch):
         flops = grid * 4 * iters * 8 * 32768
         res[name] = {"tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                      "clock_mhz": round(cyc / (ticks / 100.0)) if ticks else None}
+    # For scale: the vendor FP16 GEMM (torch.matmul -> hipBLASLt) on one large shape, random operands.
+    m, k, n = 65536, 1024, 1024
+    a = (torch.rand((m, k), device="cuda", generator=gen) * 2 - 1).to(torch.float16)
+    b = (torch.rand((k, n), device="cuda", generator=gen) * 2 - 1).to(torch.float16)
+    for _ in range(5):
+        c = a @ b
+    ms = statistics.median(time_dispatches(torch, lambda: a @ b, 20))
+    res["vendor_gemm"] = {"tflops": round(2 * m * k * n / (ms * 1e-3) / 1e12, 1), "shape": "%dx%dx%d" % (m, k, n),
+                          "library": "torch.matmul (hipBLASLt), FP16 in, FP32 accumulate"}
+    del a, b, c
     return res
 
 
