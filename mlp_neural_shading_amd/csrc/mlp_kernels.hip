@@ -312,13 +312,20 @@ struct Body {
         const int64_t row = row0 + 32 * t + n;
         const int64_t rr = row < a.batch ? row : a.batch - 1;
         constexpr int KB0 = N::KB(0);
+        // The tile's first row is the same for the whole wave: the address is a uniform base plus
+        // a 32-bit lane offset (row within the tile clamped to the batch), which the loads take as
+        // a scalar base and a vector offset, with no 64-bit address arithmetic per lane.
+        const int in_tile = 32 * t + n;
+        const int last = (int)(a.batch - 1 - row0 < NT * 32 - 1 ? a.batch - 1 - row0 : NT * 32 - 1);
+        const int r32 = in_tile < last ? in_tile : last;
 #pragma unroll
         for (int kb = 0; kb < KB0; ++kb) {
             const int c = 16 * kb + 8 * g;
             if constexpr (kVecIn) {
                 constexpr int w0 = N::w[0];
                 const int cc = (16 * kb + 16 <= w0 || c < w0) ? c : w0 - 8;  // folds for whole blocks
-                R[kb][t] = *(const h8 *)((const _Float16 *)a.x + rr * w0 + cc);
+                const char *base = (const char *)((const _Float16 *)a.x + row0 * w0);
+                R[kb][t] = *(const h8 *)(base + (unsigned)((r32 * w0 + cc) * 2));
             } else {
                 const _Float16 *xr = (const _Float16 *)a.x + rr * a.w0;
 #pragma unroll
@@ -384,7 +391,8 @@ struct Body {
                 if constexpr (kVecOut) {
                     constexpr int wl = N::w[L];
                     if (32 * mt + 8 * q < wl && c < wl)
-                        *(h4 *)((_Float16 *)a.y + row * wl + c) = __builtin_convertvector(part, h4);
+                        *(h4 *)((char *)((_Float16 *)a.y + row0 * wl) + (unsigned)(((32 * t + n) * wl + c) * 2)) =
+                            __builtin_convertvector(part, h4);
                 } else {
                     _Float16 *yr = (_Float16 *)a.y + row * a.wL;
 #pragma unroll
@@ -428,7 +436,7 @@ struct Body {
                 for (int q = 0; q < kQ; ++q) {
                     const int c = 8 * q + 4 * g;
                     if (c < wl)
-                        *(h4 *)((_Float16 *)a.y + row * wl + c) = pend.v[t][q];
+                        *(h4 *)((char *)((_Float16 *)a.y + row0 * wl) + (unsigned)(((32 * t + n) * wl + c) * 2)) = pend.v[t][q];
                 }
             }
         }
