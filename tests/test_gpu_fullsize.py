@@ -62,8 +62,9 @@ def test_page_workload_full(oracle_mod):
 
 
 # small and hetero: every row (4,096 and 1,048,576); wide (4,194,304 rows of 107,008 MACs): the first
-# and last 65,536 rows and a seeded random sample.
-@pytest.mark.parametrize("name,n_random,edge", [("small", 0, 4096), ("hetero", 0, 524288), ("wide", 16384, 65536)])
+# and last 65,536 rows and 1,048,576 seeded random rows (~1.2 M rows of the oracle, about a minute and a
+# half on a 16-core host; the whole batch would take over five minutes).
+@pytest.mark.parametrize("name,n_random,edge", [("small", 0, 4096), ("hetero", 0, 524288), ("wide", 1048576, 65536)])
 def test_full_size_sampled(oracle_mod, name, n_random, edge):
     import torch
 
@@ -78,7 +79,7 @@ def test_full_size_sampled(oracle_mod, name, n_random, edge):
 
 def test_streaming_workload_full(oracle_mod):
     """67,108,864 distinct inputs (8 GiB in, 2 GiB out): the first and last 65,536 rows, the rows whose
-    input bytes straddle each 2 GiB boundary (64-bit addressing) and 262,144 seeded random rows."""
+    input bytes straddle each 2 GiB boundary (64-bit addressing) and 1,048,576 seeded random rows."""
     import torch
 
     wl = workloads.get("stream")
@@ -90,7 +91,7 @@ def test_streaming_workload_full(oracle_mod):
     for k in (1, 2, 3):
         r = (k << 31) // row_bytes
         edges += list(range(r - 64, r + 64))
-    idx = _sample(wl, 262144, 65536, extra=edges)  # first / last 65,536 rows, 2 GiB edges, random rows
+    idx = _sample(wl, 1048576, 65536, extra=edges)  # first / last 65,536 rows, 2 GiB edges, random rows
     ref = oracle_mod.mlp_forward_rows(Ws, bs, _rows_bits(x, idx), np.arange(idx.size), threads=host_threads())
     log("   ", compare(_rows_bits(y, idx), ref, what=wl.name), "rows checked", idx.size)
     del x, y
