@@ -414,10 +414,10 @@ using NetStream = Net<64, 64, 64, 64, 64, 64, 64, 64, 16>;
 static const KernelEntry kEntries[] = {
     // (net, 32-row tiles per wave, waves per workgroup, waves per SIMD)
     entry<NetSmall, 2, 8, 2>("mlp_fused_fp8<16-32x7-4>"),
-    entry<NetPage, 2, 8, 2>("mlp_fused_fp8<32-64x7-4>"),
-    entry<NetHetero, 2, 4, 1>("mlp_fused_fp8<32-64-64-64-128-64-64-32-4>"),
-    entry<NetWide, 2, 4, 1>("mlp_fused_fp8<64-128x7-4>"),
-    entry<NetStream, 2, 8, 2>("mlp_fused_fp8<64-64x7-16>"),
+    entry<NetPage, 2, 12, 3>("mlp_fused_fp8<32-64x7-4>"),
+    entry<NetHetero, 2, 8, 2>("mlp_fused_fp8<32-64-64-64-128-64-64-32-4>"),
+    entry<NetWide, 2, 8, 2>("mlp_fused_fp8<64-128x7-4>"),
+    entry<NetStream, 2, 12, 3>("mlp_fused_fp8<64-64x7-16>"),
 };
 
 }  // namespace f8
