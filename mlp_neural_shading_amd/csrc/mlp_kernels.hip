@@ -84,6 +84,29 @@ struct BufferSource {  // image read through the caches with buffer loads (const
     }
 };
 
+// Images larger than LDS (packed layout): the whole layers that fit are staged into LDS and read
+// from there, the rest through the caches.  SPLIT is the byte offset where the cached part begins;
+// which of the two a layer uses is decided at compile time (Body::ld16), per layer.
+template <int SPLIT>
+struct HybridSource {
+    static constexpr int kSplit = SPLIT;
+    const uint8_t *base;
+    __amdgpu_buffer_rsrc_t rsrc;
+    __device__ __forceinline__ h8 lds16(int voff, int soff) const { return *(const h8 *)(base + voff + soff); }
+    __device__ __forceinline__ h8 buf16(int voff, int soff) const
+    {
+        return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
+    }
+};
+
+template <class S>
+struct is_hybrid : std::false_type {};
+template <int SPLIT>
+struct is_hybrid<HybridSource<SPLIT>> : std::true_type {};
+
+// LDS the staged weight image may use (the CU has 160 KB; a little is left for the kernel's own).
+constexpr int kLdsImageBudget = 159 * 1024;
+
 // Buffer descriptor word 3 for gfx9-family raw buffers (32-bit data format, no swizzle).
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
@@ -97,6 +120,14 @@ struct Net {
     static constexpr size_t image_bytes(int layout) { return layout == kPacked ? mlpl::pk_bytes(w, L) : mlpl::rm_bytes(w, L); }
     // Bytes of the image as staged in LDS (row-major rows are padded there).
     static constexpr size_t lds_bytes(int layout) { return layout == kPacked ? mlpl::pk_bytes(w, L) : mlpl::rml_bytes(w, L); }
+    // Packed layout: bytes of the longest run of whole layers, from layer 0, within the LDS budget.
+    static constexpr int lds_prefix()
+    {
+        int l = 0;
+        while (l < L && mlpl::pk_a_off(w, l + 1) <= (size_t)kLdsImageBudget)
+            ++l;
+        return (int)mlpl::pk_a_off(w, l);
+    }
 };
 
 template <class N, int NT, int LAYOUT, int ACT, bool GENERIC, bool LDS_W, class Src, bool DEFER>
@@ -120,12 +151,27 @@ struct Body {
 
     // ---- weight delivery ------------------------------------------------------------------
 
+    // A 16-byte read of layer l's part of the packed image; with a hybrid source, from LDS if the
+    // whole layer lies before the split, else through the caches.
+    template <int l>
+    static __device__ __forceinline__ h8 ld16(const Src &src, int voff, int soff)
+    {
+        if constexpr (is_hybrid<Src>::value) {
+            if constexpr (mlpl::pk_a_off(N::w, l + 1) <= (size_t)Src::kSplit)
+                return src.lds16(voff, soff);
+            else
+                return src.buf16(voff, soff);
+        } else {
+            return src.load16(voff, soff);
+        }
+    }
+
     template <int l>
     static __device__ __forceinline__ h8 a_frag(const Src &src, int mt, int kb, int lane)
     {
         constexpr int KB = N::KB(l);
         if constexpr (LAYOUT == kPacked) {
-            return src.load16(lane * 16, (int)mlpl::pk_a_off(N::w, l) + (mt * KB + kb) * mlpl::kFragBytes);
+            return ld16<l>(src, lane * 16, (int)mlpl::pk_a_off(N::w, l) + (mt * KB + kb) * mlpl::kFragBytes);
         } else {
             // Row-major [out][in]: lane (g, m) gathers row 32 mt + m at its slot features.  In LDS
             // the rows are padded (mlp_layout.h), in global memory they are as given.
@@ -159,10 +205,10 @@ struct Body {
         const int g = lane >> 5;
         if constexpr (LAYOUT == kPacked) {
             const int soff = (int)mlpl::pk_b_off(N::w, l) + mt * mlpl::kBiasTileBytes;
-            const f4 b0 = __builtin_bit_cast(f4, src.load16(g * 64, soff));
-            const f4 b1 = __builtin_bit_cast(f4, src.load16(g * 64 + 16, soff));
-            const f4 b2 = __builtin_bit_cast(f4, src.load16(g * 64 + 32, soff));
-            const f4 b3 = __builtin_bit_cast(f4, src.load16(g * 64 + 48, soff));
+            const f4 b0 = __builtin_bit_cast(f4, ld16<l>(src, g * 64, soff));
+            const f4 b1 = __builtin_bit_cast(f4, ld16<l>(src, g * 64 + 16, soff));
+            const f4 b2 = __builtin_bit_cast(f4, ld16<l>(src, g * 64 + 32, soff));
+            const f4 b3 = __builtin_bit_cast(f4, ld16<l>(src, g * 64 + 48, soff));
             const f8 lo = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
             const f8 hi = __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7);
             return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
@@ -530,7 +576,11 @@ __device__ __forceinline__ void stage_store_rowmajor(uint8_t *lds, const Chunks<
 template <class N, int NT, int WAVES, int EU, bool LDS_W, int LAYOUT, int ACT, bool GENERIC>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(EU, EU))) mlp_fused(LaunchArgs a)
 {
-    using Src = typename std::conditional<LDS_W, LdsSource, BufferSource>::type;
+    // Weights: the whole image in LDS (LDS_W), else the layers that fit in LDS and the rest through
+    // the caches (packed layout), else everything through the caches.
+    constexpr int kSplit = (!LDS_W && LAYOUT == kPacked) ? N::lds_prefix() : 0;
+    using Src = typename std::conditional<
+        LDS_W, LdsSource, typename std::conditional<(kSplit > 0), HybridSource<kSplit>, BufferSource>::type>::type;
     using B = Body<N, NT, LAYOUT, ACT, GENERIC, LDS_W, Src, (EU < 3 && LDS_W)>;
     constexpr int bytes = (int)N::image_bytes(LAYOUT);
     constexpr int lbytes = (int)N::lds_bytes(LAYOUT);
@@ -562,6 +612,14 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
         else
             stage_store_rowmajor<N, bytes, WAVES * 64>(lds, chunks, std::make_integer_sequence<int, kChunks>());
         src.base = lds;
+    } else if constexpr (kSplit > 0) {
+        __shared__ __attribute__((aligned(16))) uint8_t lds[kSplit];
+        constexpr int kChunks = (kSplit + WAVES * 64 * 16 - 1) / (WAVES * 64 * 16);
+        const auto chunks = stage_load<kSplit, WAVES * 64>(a.image, std::make_integer_sequence<int, kChunks>());
+        B::load_inputs(Bnext, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
+        stage_store<kSplit, WAVES * 64>(lds, chunks, std::make_integer_sequence<int, kChunks>());
+        src.base = lds;
+        src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.image, 0, bytes, kBufferRsrcWord3);
     } else {
         B::load_inputs(Bnext, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
         src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.image, 0, bytes, kBufferRsrcWord3);
