@@ -718,7 +718,7 @@ static const KernelEntry kEntries[] = {
     MLP_VARIANTS(NetSmall, 2, 8, 4, true, "16-32x7-4"),
     MLP_VARIANTS(NetPage, 2, 12, 3, true, "32-64x7-4"),
     MLP_VARIANTS(NetHetero, 2, 8, 2, true, "32-64-64-64-128-64-64-32-4"),
-    MLP_VARIANTS(NetWide, 2, 4, 1, false, "64-128x7-4"),
+    MLP_VARIANTS(NetWide, 2, 8, 2, false, "64-128x7-4"),
     MLP_VARIANTS(NetStream, 2, 12, 3, true, "64-64x7-16"),
     MLP_GENERIC(128, 128)("mlp_fused<generic128,L=1>"),
     MLP_GENERIC(128, 128, 128)("mlp_fused<generic128,L=2>"),
