@@ -123,8 +123,9 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
  *            overlap in_ptr
  *   stream   hipStream_t (NULL = the default stream)
  * Asynchronous: the buffers must stay valid until the stream's work completes.  A network beyond the
- * fused limits runs as one kernel per layer over blocks of 65,536 rows, its intermediate activations
- * in two scratch buffers (rows x the widest hidden width, padded to 32, FP16) that the call
+ * fused limits runs as one kernel per layer over blocks of rows (as many as make the scratch below
+ * 512 MiB, at least 65,536), its intermediate activations in two scratch buffers (block rows x the
+ * widest hidden width, padded to 32, FP16) that the call
  * allocates and frees in order on `stream` from a memory pool the library keeps (so calls on
  * different streams never share them); MLP_ERR_OUT_OF_MEMORY if they cannot be allocated.  Must be called
  * with the device that was current at pack time.  Uses the activation form set by

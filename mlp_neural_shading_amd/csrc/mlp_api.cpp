@@ -66,8 +66,12 @@ const KernelEntry kLayered = {"mlp_layered<gemm 128x128, fused epilogue>", 0, {}
                               MLP_ACT_VECTOR, 256, 128, true, nullptr, nullptr};
 bool is_layered(const KernelEntry *e) { return e == &kLayered; }
 
-// Rows per pass of the layered path (its scratch holds two such blocks of activations).
-constexpr int64_t kLayeredChunkRows = 65536;
+// Rows per pass of the layered path: as many as two blocks of activations at the widest hidden
+// layer fit in kLayeredScratchBytes, and at least kLayeredMinRows.  Larger passes mean fewer
+// launches, each with more workgroups than the GPU holds at once (a launch of one round of
+// workgroups pays a whole tail).
+constexpr int64_t kLayeredMinRows = 65536;
+constexpr int64_t kLayeredScratchBytes = (int64_t)512 << 20;
 
 // Device memory for the layered path's intermediate activations: a pool owned by the library with
 // no release threshold, so that the stream-ordered allocation of each call reuses memory.
@@ -376,7 +380,7 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
 
 namespace {
 
-// The layered path: rows in blocks of kLayeredChunkRows, each block through every layer, with the
+// The layered path: rows in blocks (see kLayeredScratchBytes), each block through every layer, with the
 // activations between layers in two scratch buffers allocated on the stream (stream-ordered, so
 // calls on different streams never share them) and freed on it afterwards.
 int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t stream)
@@ -386,7 +390,9 @@ int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t 
     int ld_max = 0;  // row stride of the scratch buffers: the widest hidden layer, padded to 32 halves
     for (int l = 1; l < L; ++l)
         ld_max = mlpk::layered_kin(w[l]) > ld_max ? mlpk::layered_kin(w[l]) : ld_max;
-    const int64_t chunk = batch < kLayeredChunkRows ? batch : kLayeredChunkRows;
+    int64_t block = kLayeredScratchBytes / (2 * 2 * (int64_t)(ld_max > 0 ? ld_max : 1)) / 128 * 128;
+    block = block > kLayeredMinRows ? block : kLayeredMinRows;
+    const int64_t chunk = batch < block ? batch : block;
     void *buf[2] = {nullptr, nullptr};
     if (L > 1) {
         hipMemPool_t pool = nullptr;

@@ -47,7 +47,8 @@ def test_random_nets(oracle_mod, widths, rows):
 
 
 def test_more_than_one_block_of_rows(oracle_mod):
-    widths = (160, 16, 8)
+    # a 4096-wide hidden layer keeps the pass at its minimum of 65,536 rows: two passes
+    widths = (64, 4096, 8)
     rows = 65536 + 777
     Ws, bs = workloads.init_weights(widths, seed=9)
     x = _x(rows, widths[0], 4)
