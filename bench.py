@@ -495,24 +495,33 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
-    # The timed region: exactly --steps back-to-back steps, synchronised on both sides.
+    # The timed region: exactly --steps back-to-back steps, synchronised on both sides.  Two HIP
+    # events on the launch stream bracket the same region: their interval over --steps is the
+    # average launch duration on the GPU (the kernels run back to back, so it is the kernel time
+    # plus the gap between consecutive kernels).
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for _ in range(args.steps):
         step()
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # The same steps again, each bracketed by HIP events on the launch stream: kernel durations.
-    launch_ms = time_dispatches(torch, step, args.steps)
-    mean_launch_ms = statistics.fmean(launch_ms)
+    mean_launch_ms = ev0.elapsed_time(ev1) / args.steps
     achieved_tflops = flops_per_launch / (mean_launch_ms * 1e-3) / 1e12
+    # The same steps again, each alone between its own pair of events (which adds the dispatch
+    # latency between the first event and the kernel to every interval): reported for reference.
+    launch_ms = time_dispatches(torch, step, args.steps)
 
     traffic = load_traffic(wl.name, kernel)
     roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": PEAK_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP16_TFLOPS, 4), "traffic": traffic,
                 "kernel": kernel, "mean_launch_ms": round(mean_launch_ms, 6),
-                "median_launch_ms": round(statistics.median(launch_ms), 6),
+                "isolated_launch_ms": {"mean": round(statistics.fmean(launch_ms), 6),
+                                       "median": round(statistics.median(launch_ms), 6),
+                                       "min": round(min(launch_ms), 6)},
                 "io_gbs": round(wl.io_bytes_per_eval * wl.batch / (mean_launch_ms * 1e-3) / 1e9, 1)}
 
     dispatch = {"empty_kernel_ms": round(measure_empty_dispatch(torch, roofline_grid(B, wl)), 6),
