@@ -330,8 +330,9 @@ def measure_device_pack(torch, B, wl, Ws, bs) -> float:
 
 def measure_ceiling(torch):
     """FP16 MFMA throughput the device sustains on random operands (v_mfma_f32_32x32x16_f16 loop,
-    4 waves per SIMD), alone and with 6 packed-FP16 VALU instructions per MFMA, and on all-zero
-    operands (which switch little and so let the clock stay high); see mlp_ceiling.h."""
+    4 waves per SIMD), alone and with 6 or 7 packed-FP16 VALU instructions per MFMA (the fused kernel
+    issues between the two), and on all-zero operands (which switch little and so let the clock stay
+    high); see mlp_ceiling.h."""
     lib = ceiling_lib()
     props = torch.cuda.get_device_properties(0)
     grid = props.multi_processor_count * 4
@@ -343,7 +344,7 @@ def measure_ceiling(torch):
     stream = torch.cuda.current_stream()
     res = {}
     for name, operands, k in (("valu_per_mfma_0", random_ops, 0), ("valu_per_mfma_6", random_ops, 6),
-                              ("zero_operands", zero_ops, 0)):
+                              ("valu_per_mfma_7", random_ops, 7), ("zero_operands", zero_ops, 0)):
         iters = 20000
 
         def run():

@@ -14,7 +14,7 @@ extern "C" {
 
 /* Enqueue one launch of a loop of independent v_mfma_f32_32x32x16_f16 instructions (8 per iteration,
  * each 32,768 FLOP) on `stream`, 256 threads per workgroup.
- *   valu_per_mfma  0 or 6: independent packed-FP16 VALU instructions issued after each MFMA
+ *   valu_per_mfma  0, 6 or 7: independent packed-FP16 VALU instructions issued after each MFMA
  *   grid           workgroups (4 per compute unit = 4 waves per SIMD)
  *   operands       device buffer of at least 32,768 bytes of FP16 data (the MFMA operands)
  *   out            device buffer of grid * 256 floats (keeps the results live)
