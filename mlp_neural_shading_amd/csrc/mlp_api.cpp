@@ -62,8 +62,8 @@ int g_act_mode = MLP_ACT_VECTOR;
 
 // The layer-by-layer path (mlp_layered.hip) stands in the registry's place for shapes no fused kernel
 // serves: widths above MLP_FUSED_MAX_WIDTH or more than MLP_FUSED_MAX_LAYERS layers.
-const KernelEntry kLayered = {"mlp_layered<gemm 128x128, fused epilogue>", 0, {}, true, MLP_LAYOUT_PACKED,
-                              MLP_ACT_VECTOR, 256, 128, true, nullptr, nullptr};
+const KernelEntry kLayered = {"mlp_layered<gemm 128x256, fused epilogue>", 0, {}, true, MLP_LAYOUT_PACKED,
+                              MLP_ACT_VECTOR, 256, 64, true, nullptr, nullptr};
 bool is_layered(const KernelEntry *e) { return e == &kLayered; }
 
 // Rows per pass of the layered path: as many as two blocks of activations at the widest hidden
@@ -387,10 +387,11 @@ int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t 
 {
     const int L = g_net.n_layers;
     const int *w = g_net.widths;
-    int ld_max = 0;  // row stride of the scratch buffers: the widest hidden layer, padded to 32 halves
+    int ld_max = 0;  // row stride of the scratch buffers: the widest hidden layer, padded to 64 halves
     for (int l = 1; l < L; ++l)
         ld_max = mlpk::layered_kin(w[l]) > ld_max ? mlpk::layered_kin(w[l]) : ld_max;
-    int64_t block = kLayeredScratchBytes / (2 * 2 * (int64_t)(ld_max > 0 ? ld_max : 1)) / 128 * 128;
+    const int64_t tile = mlpk::layered_rows_per_tile();
+    int64_t block = kLayeredScratchBytes / (2 * 2 * (int64_t)(ld_max > 0 ? ld_max : 1)) / tile * tile;
     block = block > kLayeredMinRows ? block : kLayeredMinRows;
     const int64_t chunk = batch < block ? batch : block;
     void *buf[2] = {nullptr, nullptr};

@@ -8,9 +8,10 @@
 
 namespace mlpk {
 
-// Padded widths of the layered image: every layer's K (input width) to a multiple of 32, every
-// layer's M (output width) to a multiple of 128 (the kernel's workgroup tile).
-inline int layered_kin(int w) { return (w + 31) / 32 * 32; }
+// Padded widths of the layered image: every layer's K (input width) to a multiple of 64 (an even
+// number of the kernel's 32-deep K steps), every layer's M (output width) to a multiple of 128 (the
+// kernel's workgroup tile).
+inline int layered_kin(int w) { return (w + 63) / 64 * 64; }
 inline int layered_kout(int w) { return (w + 127) / 128 * 128; }
 
 // Per layer l, in order: A fragments [kout/32][kin/16][64 lanes][8 halves] (natural K order: slot
@@ -29,7 +30,7 @@ struct LayerArgs {
     const uint8_t *a;   // this layer's A fragments
     const float *bias;  // this layer's bias tiles
     int64_t rows;
-    int64_t row_tiles;  // ceil(rows / 128)
+    int64_t row_tiles;  // ceil(rows / layered_rows_per_tile())
     int win, wout;      // real widths
     int kin, kout;      // padded widths (layered_kin / layered_kout)
     int act;            // 1: leaky ReLU after the rounding; 0: none (last layer)

@@ -9,18 +9,21 @@
 // setup" and "Bad versus good activation"), with the activations between layers in device memory.
 //
 // Tiling (v_mfma_f32_32x32x16_f16, weights = A operand, rows = B operand, as in the fused kernel):
-//   - a workgroup (4 waves) computes 128 outputs x 128 rows; wave (wm, wn) the 64 x 64 quarter
-//     (wm, wn), i.e. 2 x 2 MFMA tiles, so every A and B fragment read from LDS feeds two MFMAs;
-//   - K advances 32 at a time; the next 32 are loaded from global memory into registers while the
-//     current ones are multiplied, then written to the other half of a double-buffered LDS tile;
-//   - the weight image is fragment-ordered per layer (natural K order: slot (kb, g, j) = feature
-//     16 kb + 8 g + j), so a fragment is one 16-byte LDS read per lane; the activation tile is kept
-//     as rows of 32 halves padded to 40 (80-byte stride: 16 consecutive rows start 4 banks apart,
-//     "Optimization Techniques", "Avoiding Bank Conflicts");
+//   - a workgroup (4 waves) computes 128 outputs x 256 rows; each wave owns 64 rows (two 32-row
+//     sample tiles) and all 128 outputs (four output tiles), so every A fragment read from LDS feeds
+//     two MFMAs and every B fragment four;
+//   - the rows are the B operand straight from global memory: lane (g, n) loads the 16 bytes of row
+//     n at columns 16 kb + 8 g .. + 8, one K step ahead, so activations never pass through LDS (no
+//     other wave uses them).  Rows past the batch load the last row instead; their outputs are
+//     never stored, and each output row depends on its own input row only;
+//   - the weights are shared by the four waves through a double-buffered LDS tile, K advancing 32 at
+//     a time: the next step's tile is loaded into registers while the current one is multiplied;
+//     the weight image is fragment-ordered per layer (natural K order: slot (kb, g, j) = feature
+//     16 kb + 8 g + j), so a fragment is one 16-byte LDS read per lane;
 //   - the bias is the C operand of the first MFMA of each output tile; the epilogue converts FP32 ->
 //     FP16 (nearest even), applies the leaky ReLU on packed FP16 and stores 4 outputs per lane.
 //   - workgroups are numbered so that each XCD takes a contiguous run of (row tile, output tile)
-//     pairs, output tiles fastest: the workgroups that share a row tile share that XCD's L2.
+//     pairs, output tiles fastest: the workgroups that read the same rows share that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include "mlp_layered.h"
@@ -35,24 +38,21 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16x __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128;         // outputs per workgroup
-constexpr int kBN = 128;         // rows per workgroup
+constexpr int kBN = 256;         // rows per workgroup (64 per wave)
 constexpr int kBK = 32;          // K per step
 constexpr int kThreads = 256;    // 4 waves
-constexpr int kRowHalves = 40;   // LDS row of the activation tile: 32 halves + 8 of padding
 constexpr int kABytes = (kBM / 32) * (kBK / 16) * 1024;  // 8 fragments of 1 KB
-constexpr int kBBytes = kBN * kRowHalves * 2;            // 10 KB
 
 __device__ __forceinline__ _Float16 slope() { return __builtin_bit_cast(_Float16, (unsigned short)0x211f); }
 
-// One 16-byte chunk (8 halves) of row `row`, columns c .. c+7 of X; zero past the rows or columns.
-__device__ __forceinline__ h8 load_x8(const LayerArgs &p, int64_t row, int c)
+// One 16-byte chunk (8 halves) of a row, columns c .. c+7; zero past the row's win columns.  WHOLE:
+// the rows are 16-byte aligned and win equals the padded K, so every chunk is one load.
+template <bool WHOLE>
+__device__ __forceinline__ h8 load_x8(const LayerArgs &p, const _Float16 *xr, int c)
 {
-    h8 v = (h8)(_Float16)0;
-    if (row >= p.rows)
-        return v;
-    const _Float16 *xr = (const _Float16 *)p.x + row * p.ldx;
-    if (p.vec_x && c + 8 <= p.win)
+    if (WHOLE || (p.vec_x && c + 8 <= p.win))
         return *(const h8 *)(xr + c);
+    h8 v = (h8)(_Float16)0;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         if (c + j < p.win)
@@ -60,13 +60,12 @@ __device__ __forceinline__ h8 load_x8(const LayerArgs &p, int64_t row, int c)
     return v;
 }
 
-// Four waves per SIMD (128 registers, no spills; four 36 KB workgroups per CU): more workgroups
-// in flight hide more of the operand loads' latency (-2.5 % on 1024-wide layers, -4 % on 256-wide
-// ones against three).
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void layer_gemm(LayerArgs p)
+// Two waves per SIMD: the 128 accumulator registers, two steps of B fragments and the A fragments
+// need ~200 registers per lane.
+template <bool WHOLE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void layer_gemm(LayerArgs p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kABytes];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kBBytes];
 
     // Workgroup -> (row tile, output tile): XCD x = b % 8 takes the x-th contiguous run of tiles.
     const int64_t n_out = p.kout / kBM;
@@ -80,44 +79,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     const int64_t row0 = rt * kBN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
     const int g = lane >> 5, n = lane & 31;
     const int KB = p.kin / 16;  // fragments per output tile of the image
     const int steps = p.kin / kBK;
 
-    // Global sources of this thread's share of a K step: two A chunks and two B chunks of 16 bytes.
-    //   A: chunk q = tid + 256 i (i = 0, 1) of the 8 KB tile: fragment f = q / 64 = (mt, kb) with
-    //      mt = f / 2, kb = f % 2, lane slice q % 64 (the LDS tile keeps this order).
-    //   B: row s = tid / 2, columns 16 (tid % 2) + 8 i.
+    // This thread's share of a K step of the weight tile: chunk q = tid + 256 i (i = 0, 1) of the
+    // 8 KB tile, fragment f = q / 64 = (mt, kb) with mt = f / 2, kb = f % 2, lane slice q % 64 (the
+    // LDS tile keeps this order).
     const uint8_t *a_tile = p.a + (size_t)(ot * (kBM / 32)) * KB * 1024;
-    const int bs = tid >> 1, bc = (tid & 1) * 16;
+    const int fa0 = tid >> 6, fa1 = (tid + kThreads) >> 6;
+    const size_t lane16 = (size_t)(tid & 63) * 16;
+    // This lane's two rows (sample tiles j = 0, 1), clamped to the batch.
+    const _Float16 *xr[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t row = row0 + 64 * wave + 32 * j + n;
+        xr[j] = (const _Float16 *)p.x + (row < p.rows ? row : p.rows - 1) * p.ldx;
+    }
 
     // Named registers rather than arrays indexed in helper lambdas: the compiler placed those in
-    // scratch memory.
+    // scratch memory.  The weight loads are issued before the row loads, so the LDS store of the
+    // weights waits for them alone.
     uint4 ra0, ra1;
-    h8 rb0, rb1;
-    const int fa0 = tid >> 6, fa1 = (tid + kThreads) >> 6;  // fragments (mt, kb) = (f >> 1, f & 1)
-    const size_t lane16 = (size_t)(tid & 63) * 16;
-#define MLPL_LOAD_STEP(step)                                                                                   \
+    h8 bc[2][2], bn[2][2];  // [kb][j]: B fragments of the even and the odd K steps
+#define MLPL_LOAD_A(step)                                                                                      \
     do {                                                                                                       \
         ra0 = *(const uint4 *)(a_tile + ((size_t)(fa0 >> 1) * KB + (step) * 2 + (fa0 & 1)) * 1024 + lane16);  \
         ra1 = *(const uint4 *)(a_tile + ((size_t)(fa1 >> 1) * KB + (step) * 2 + (fa1 & 1)) * 1024 + lane16);  \
-        rb0 = load_x8(p, row0 + bs, (step) * kBK + bc);                                                        \
-        rb1 = load_x8(p, row0 + bs, (step) * kBK + bc + 8);                                                    \
     } while (0)
-#define MLPL_STORE_STEP(buf)                                                                                   \
+#define MLPL_LOAD_B(dst, step)                                                                                 \
+    do {                                                                                                       \
+        _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                                       \
+            _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                      \
+                dst[kb][j] = load_x8<WHOLE>(p, xr[j], (step) * kBK + 16 * kb + 8 * g);                                \
+    } while (0)
+#define MLPL_STORE_A(buf)                                                                                      \
     do {                                                                                                       \
         *(uint4 *)(lds_a[buf] + tid * 16) = ra0;                                                               \
         *(uint4 *)(lds_a[buf] + (tid + kThreads) * 16) = ra1;                                                  \
-        *(h8 *)(lds_b[buf] + (bs * kRowHalves + bc) * 2) = rb0;                                                \
-        *(h8 *)(lds_b[buf] + (bs * kRowHalves + bc + 8) * 2) = rb1;                                            \
     } while (0)
 
-    // Bias tiles of this wave's two output tiles (the C operand of the first MFMA).
-    f16x acc[2][2];
+    // Bias tiles of the four output tiles (the C operand of the first MFMA).
+    f16x acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int mtg = ot * (kBM / 32) + 2 * wm + i;  // output tile in the layer
+    for (int i = 0; i < 4; ++i) {
+        const int mtg = ot * (kBM / 32) + i;  // output tile in the layer
         const f4 *bt = (const f4 *)(p.bias + mtg * 32 + g * 16);
         const f4 b0 = bt[0], b1 = bt[1], b2 = bt[2], b3 = bt[3];
         f16x b;
@@ -132,41 +138,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
         acc[i][1] = b;
     }
 
-    MLPL_LOAD_STEP(0);
-    MLPL_STORE_STEP(0);
-    __syncthreads();
-    for (int step = 0; step < steps; ++step) {
-        const int buf = step & 1;
-        if (step + 1 < steps)
-            MLPL_LOAD_STEP(step + 1);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            h8 af[2], bf[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[i] = *(const h8 *)(lds_a[buf] + (((2 * wm + i) * 2 + kb) * 64 + lane) * 16);
-                bf[i] = *(const h8 *)(lds_b[buf] + ((64 * wn + 32 * i + n) * kRowHalves + kb * 16 + 8 * g) * 2);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        if (step + 1 < steps) {
-            MLPL_STORE_STEP(buf ^ 1);
-            __syncthreads();
-        }
-    }
+    // One K step: multiply with CUR (this step's B fragments) and the LDS tile `buf`.  A step with a
+    // successor first requests the next step's weights and rows (rows into NXT) and ends by storing
+    // those weights into the other LDS tile.  The K loop alternates the two B buffers and has no
+    // branch inside, so no fragment is copied and each row load is first waited for where it is used.
+    // Scheduling barriers hold the loads at the top of the step and the LDS store at its end:
+    // otherwise the compiler moves them next to each other and the store waits a full round trip.
+#define MLPL_MFMAS(step, CUR)                                                                                  \
+    do {                                                                                                       \
+        const int buf = (step) & 1;                                                                            \
+        _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                                       \
+        {                                                                                                      \
+            h8 af[4];                                                                                          \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                      \
+                af[i] = *(const h8 *)(lds_a[buf] + ((i * 2 + kb) * 64 + lane) * 16);                           \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                      \
+                _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                  \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], CUR[kb][j], acc[i][j], 0, 0, 0); \
+        }                                                                                                      \
+    } while (0)
+#define MLPL_STEP(step, CUR, NXT)                                                                              \
+    do {                                                                                                       \
+        MLPL_LOAD_A((step) + 1);                                                                               \
+        MLPL_LOAD_B(NXT, (step) + 1);                                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                                     \
+        MLPL_MFMAS(step, CUR);                                                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                                     \
+        MLPL_STORE_A(((step) & 1) ^ 1);                                                                        \
+        __syncthreads();                                                                                       \
+    } while (0)
 
-    // Epilogue: lane (g, n) holds, for row 64 wn + 32 j + n, outputs 32 mt + 8 q + 4 g + i.
+    // kin is a multiple of 64, so the number of steps is even (and at least 2).
+    MLPL_LOAD_A(0);
+    MLPL_LOAD_B(bc, 0);
+    MLPL_STORE_A(0);
+    __syncthreads();
+    for (int step = 0; step + 2 < steps; step += 2) {
+        MLPL_STEP(step, bc, bn);
+        MLPL_STEP(step + 1, bn, bc);
+    }
+    MLPL_STEP(steps - 2, bc, bn);
+    MLPL_MFMAS(steps - 1, bn);
+
+    // Epilogue: lane (g, n) holds, for row 64 wave + 32 j + n, outputs 32 mt + 8 q + 4 g + i.
     const h4 s4 = (h4)slope();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int cbase = (ot * (kBM / 32) + 2 * wm + i) * 32 + 4 * g;
+    for (int i = 0; i < 4; ++i) {
+        const int cbase = (ot * (kBM / 32) + i) * 32 + 4 * g;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int64_t row = row0 + 64 * wn + 32 * j + n;
+            const int64_t row = row0 + 64 * wave + 32 * j + n;
             if (row >= p.rows)
                 continue;
             _Float16 *yr = (_Float16 *)p.y + row * p.ldy;
@@ -188,8 +209,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
             }
         }
     }
-#undef MLPL_LOAD_STEP
-#undef MLPL_STORE_STEP
+#undef MLPL_LOAD_A
+#undef MLPL_LOAD_B
+#undef MLPL_STORE_A
+#undef MLPL_MFMAS
+#undef MLPL_STEP
 }
 
 }  // namespace
@@ -197,7 +221,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 hipError_t launch_layer(const LayerArgs &p, hipStream_t stream)
 {
     const int64_t tiles = p.row_tiles * (p.kout / kBM);
-    hipLaunchKernelGGL(layer_gemm, dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(kThreads), 0, stream, p);
+    const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
+    if (p.vec_x && p.win == p.kin)
+        hipLaunchKernelGGL(layer_gemm<true>, grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(layer_gemm<false>, grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -120,12 +120,12 @@ def test_plan_widths():
     assert B.mlp_plan_widths(workloads.get("hetero").widths) == [32, 64, 64, 64, 128, 64, 64, 32, 32]
     assert B.mlp_plan_widths([2, 2, 1]) == [128, 128, 128]  # generic kernel, zero-padded
     assert B.mlp_plan_widths([100, 300, 129, 7]) == [128, 384, 256, 128]  # layer by layer
-    assert B.mlp_plan_widths([16] * 10) == [32] + [128] * 9
+    assert B.mlp_plan_widths([16] * 10) == [64] + [128] * 9
 
 
 # ---- an independent reading of the layer-by-layer image ------------------------------------------
 #
-# Per layer: A fragments [MT][KB][lane][8] with MT = ceil(w_out / 128) * 4, KB = ceil(w_in / 32) * 2,
+# Per layer: A fragments [MT][KB][lane][8] with MT = ceil(w_out / 128) * 4, KB = ceil(w_in / 64) * 4,
 # lane = 32 g + m holding row 32 mt + m and input features 16 kb + 8 g + j (natural order); then the
 # bias tiles [MT][g][16] FP32 with entry (mt, g, j) = b[32 mt + 8 (j // 4) + 4 g + j % 4].
 
@@ -134,7 +134,7 @@ def _unpack_layered(image, widths):
     Ws, bs = [], []
     for l in range(len(widths) - 1):
         MT = -(-widths[l + 1] // 128) * 4
-        KB = -(-widths[l] // 32) * 2
+        KB = -(-widths[l] // 64) * 4
         A = image[off:off + MT * KB * 1024].view(np.uint16).reshape(MT, KB, 2, 32, 8)
         off += MT * KB * 1024
         bias = image[off:off + MT * 128].view(np.float32).reshape(MT, 2, 16)
