@@ -18,7 +18,7 @@ inference", section "Experiment setup").  Prints one JSON line:
   dispatch     an empty kernel timed the same way, and the wall-clock gap between back-to-back steps
   overlap      mlp_infer on a second stream beside a copy or a GEMM: alone, serial and concurrent times
   layered      networks beyond the fused kernels (widths > 128, more than 8 layers), layer by layer
-  clocks       the GPU clocks reported by rocm-smi before and after the measurements
+  clocks       the GPU clock levels the driver reports before and after the measurements
   cpu_baseline the CPU oracle on a bounded sample of the same rows, one host thread pinned to a core
 """
 from __future__ import annotations
@@ -266,19 +266,17 @@ def measure_layered(torch, B, workloads) -> dict:
     res = {}
     dev = torch.device("cuda:0")
     sh = torch.cuda.current_stream().cuda_stream
-    for widths, rows in (((64,) + (1024,) * 7 + (16,), 65536), ((256,) * 17, 262144)):
-        Ws, bs = workloads.init_weights(widths, seed=1)
-        gen = torch.Generator(device=dev).manual_seed(3)
-        x = (torch.rand((rows, widths[0]), device=dev, generator=gen) * 2 - 1).to(torch.float16)
+    for name, wl in workloads.LAYERED.items():
+        widths, rows = wl.widths, wl.batch
+        Ws, bs = wl.weights()
+        x = wl.inputs(device=dev)
         y = torch.empty((rows, widths[-1]), dtype=torch.float16, device=dev)
         B.mlp_pack_weights(Ws, bs, B.MLP_LAYOUT_PACKED, sh)
         f = lambda: B.mlp_infer(rows, x.data_ptr(), y.data_ptr(), sh)
         for _ in range(3):
             f()
         ms = statistics.median(time_dispatches(torch, f, 10))
-        flops = 2 * rows * sum(widths[l] * widths[l + 1] for l in range(len(widths) - 1))
-        tflops = flops / (ms * 1e-3) / 1e12
-        name = "mlp%d-%s-b%d" % (len(widths) - 1, "-".join(str(w) for w in widths), rows)
+        tflops = wl.flops_per_eval * rows / (ms * 1e-3) / 1e12
         res[name] = {"median_ms": round(ms, 4), "m_evals_per_s": round(throughput_m_evals(rows, ms), 1),
                      "tflops": round(tflops, 1), "frac_fp16_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
                      "kernel": B.mlp_kernel_name(B.MLP_ACT_VECTOR)}
@@ -288,15 +286,25 @@ def measure_layered(torch, B, workloads) -> dict:
 
 
 def read_clocks() -> dict:
-    """Current SCLK / MCLK as rocm-smi reports them (best effort; the clocks cannot be locked here)."""
-    import subprocess
+    """Current SCLK / MCLK levels from the amdgpu driver's DPM tables in sysfs (the level marked with
+    '*'), read in this process with no helper program; best effort, since the clocks cannot be locked
+    here.  With several cards visible, the first one that has the tables is read."""
+    import glob
+
+    def current(path):
+        for line in Path(path).read_text().splitlines():
+            if line.rstrip().endswith("*"):
+                level, freq = line.split(":", 1)
+                return {"level": int(level), "freq": freq.replace("*", "").strip()}
+        return None
 
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
-        data = json.loads(r.stdout)
-        card = next(iter(data.values()))
-        return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()}
-    except Exception as e:  # the tool may be missing or print something else
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            if os.path.exists(dev + "/pp_dpm_sclk"):
+                return {"card": dev.split("/")[-2], "sclk": current(dev + "/pp_dpm_sclk"),
+                        "mclk": current(dev + "/pp_dpm_mclk") if os.path.exists(dev + "/pp_dpm_mclk") else None}
+        return {"error": "no amdgpu DPM tables under /sys/class/drm"}
+    except (OSError, ValueError) as e:
         return {"error": "%s: %s" % (type(e).__name__, str(e)[:200])}
 
 
@@ -403,7 +411,7 @@ def cpu_baseline(wl, Ws, bs, x_dev, rows: int):
         os.sched_setaffinity(0, allowed)
     return {"value": round(throughput_m_evals(rows, dt * 1e3), 6), "unit": "M evals/s", "cores": 1,
             "kind": "oracle",
-            "sample": "first %d of the %d rows (all %d distinct inputs), single-threaded C oracle (gcc %s) pinned "
+            "sample": "first %d of the %d rows (%d distinct inputs in the batch), single-threaded C oracle (gcc %s) pinned "
                       "to CPU %d of %d visible, %.1f s on %s"
                       % (rows, wl.batch, wl.unique_rows, " ".join(oracle.CFLAGS[:4]), core, len(allowed), dt,
                          cpu_model())}
@@ -468,10 +476,14 @@ def main() -> int:
     from mlp_neural_shading_amd import binding as B
     from mlp_neural_shading_amd import workloads
 
+    wl = workloads.get(args.workload)
+    layered_net = wl.name in workloads.LAYERED  # runs layer by layer: packed FP16 only, no A/B variants
+    if layered_net and args.layout != "packed":
+        print("%s runs layer by layer, which only the packed layout serves" % wl.name, file=sys.stderr)
+        return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     clocks_before = read_clocks()
-    wl = workloads.get(args.workload)
     Ws, bs = wl.weights()
     x = wl.inputs(device=dev)
     y = torch.empty((wl.batch, wl.widths[-1]), dtype=torch.float16, device=dev)
@@ -529,7 +541,7 @@ def main() -> int:
                 "step_minus_kernel_ms": round(ms_per_step - mean_launch_ms, 6)}
 
     variants = {}
-    if not args.no_variants:
+    if not args.no_variants and not layered_net:
         variants = summarise_variants(protocol_variants(wl.name), wl)
 
     if not args.no_ceiling:
@@ -546,13 +558,17 @@ def main() -> int:
     layered = {}
     if not args.no_workloads:
         per_workload = measure_workloads(torch, B, workloads, skip=wl.name)
-        per_workload[wl.name]["variants"] = variants
+        if wl.name in per_workload:
+            per_workload[wl.name]["variants"] = variants
         layered = measure_layered(torch, B, workloads)
     clocks_after = read_clocks()
 
     cpu = None
     if args.cpu_rows > 0:
-        cpu = cpu_baseline(wl, Ws, bs, x, min(args.cpu_rows, wl.unique_rows))
+        # A bounded sample: at most --cpu-rows rows and at most the FLOPs of 65,536 rows of the
+        # page-shaped network (~3.5 GFLOP, ~20 s for the oracle), so wide networks stay short too.
+        rows = min(args.cpu_rows, wl.unique_rows, max(64, 65536 * 53760 // wl.flops_per_eval))
+        cpu = cpu_baseline(wl, Ws, bs, x, rows)
 
     out = {
         "metric": METRIC,

@@ -34,3 +34,26 @@ def test_more_than_one_gpu_is_refused():
 def test_throughput_arithmetic():
     # 1,048,576 evaluations in 0.0524288 ms = 20,000 M evals/s
     assert abs(bench.throughput_m_evals(1 << 20, 0.0524288) - 20000.0) < 1e-6
+
+
+def test_layered_workloads_are_named_apart():
+    from mlp_neural_shading_amd import binding as B
+    from mlp_neural_shading_amd import workloads
+
+    wide = workloads.get("layered1024")
+    assert wide.widths == (64,) + (1024,) * 7 + (16,) and wide.batch == 65536
+    deep = workloads.get("layered256")
+    assert deep.widths == (256,) * 17 and deep.batch == 262144
+    # the fused workloads' tables (which the FP8 and row-major tests iterate) do not list them
+    assert not set(workloads.LAYERED) & set(workloads.WORKLOADS)
+    assert not set(workloads.LAYERED_ALIASES) & set(workloads.ALIASES)
+    # both run layer by layer: every width padded to the layered tiles
+    assert B.mlp_plan_widths(wide.widths) == [64] + [1024] * 7 + [128]
+    assert B.mlp_plan_widths(deep.widths) == [256] * 17
+
+
+def test_layered_workload_refuses_the_row_major_layout():
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--workload", "layered1024", "--layout", "rowmajor"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "packed layout" in r.stderr
