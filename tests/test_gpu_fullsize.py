@@ -77,6 +77,22 @@ def test_full_size_sampled(oracle_mod, name, n_random, edge):
     log("   ", compare(_rows_bits(y, idx), ref, what=wl.name), "rows checked", idx.size)
 
 
+# The layer-by-layer networks at the sizes the benchmark times (one block of rows each, every layer a
+# separate GEMM launch): the first and last row tiles and seeded random rows against the oracle
+# (the 1024-wide net costs ~6.4 M multiply-adds per row on the host, the 256-wide one ~1 M).
+@pytest.mark.parametrize("name,n_random,edge", [("layered1024", 1024, 256), ("layered256", 4096, 1024)])
+def test_layered_workload_full_size_sampled(oracle_mod, name, n_random, edge):
+    import torch
+
+    wl = workloads.get(name)
+    log("full", wl.name, B.mlp_plan_widths(wl.widths))
+    Ws, bs, x, y = _run_full(wl)
+    assert bool(torch.isfinite(y).all())
+    idx = _sample(wl, n_random, edge)
+    ref = oracle_mod.mlp_forward_rows(Ws, bs, _rows_bits(x, idx), np.arange(idx.size), threads=host_threads())
+    log("   ", compare(_rows_bits(y, idx), ref, what=wl.name), "rows checked", idx.size)
+
+
 def test_streaming_workload_full(oracle_mod):
     """67,108,864 distinct inputs (8 GiB in, 2 GiB out): the first and last 65,536 rows, the rows whose
     input bytes straddle each 2 GiB boundary (64-bit addressing) and 1,048,576 seeded random rows."""
