@@ -17,7 +17,8 @@
 //     other wave uses them).  Rows past the batch load the last row instead; their outputs are
 //     never stored, and each output row depends on its own input row only;
 //   - the weights are shared by the four waves through a double-buffered LDS tile, K advancing 32 at
-//     a time: the next step's tile is loaded into registers while the current one is multiplied;
+//     a time: each step's tile is requested two steps ahead into one of two sets of staging
+//     registers and stored into LDS at the end of the step before it is used;
 //     the weight image is fragment-ordered per layer (natural K order: slot (kb, g, j) = feature
 //     16 kb + 8 g + j), so a fragment is one 16-byte LDS read per lane;
 //   - the bias is the C operand of the first MFMA of each output tile; the epilogue converts FP32 ->
@@ -60,8 +61,8 @@ __device__ __forceinline__ h8 load_x8(const LayerArgs &p, const _Float16 *xr, in
     return v;
 }
 
-// Two waves per SIMD: the 128 accumulator registers, two steps of B fragments and the A fragments
-// need ~200 registers per lane.
+// Two waves per SIMD: the 128 accumulator registers, two steps of B fragments, the eight A fragments
+// of a step and two sets of weight staging need ~240 registers per lane.
 template <bool WHOLE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void layer_gemm(LayerArgs p)
 {
@@ -100,12 +101,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Named registers rather than arrays indexed in helper lambdas: the compiler placed those in
     // scratch memory.  The weight loads are issued before the row loads, so the LDS store of the
     // weights waits for them alone.
-    uint4 ra0, ra1;
+    uint4 ra0, ra1, rb0, rb1;  // weight staging of the even (ra) and the odd (rb) K steps
     h8 bc[2][2], bn[2][2];  // [kb][j]: B fragments of the even and the odd K steps
-#define MLPL_LOAD_A(step)                                                                                      \
+#define MLPL_LOAD_A(R0, R1, step)                                                                              \
     do {                                                                                                       \
-        ra0 = *(const uint4 *)(a_tile + ((size_t)(fa0 >> 1) * KB + (step) * 2 + (fa0 & 1)) * 1024 + lane16);  \
-        ra1 = *(const uint4 *)(a_tile + ((size_t)(fa1 >> 1) * KB + (step) * 2 + (fa1 & 1)) * 1024 + lane16);  \
+        R0 = *(const uint4 *)(a_tile + ((size_t)(fa0 >> 1) * KB + (step) * 2 + (fa0 & 1)) * 1024 + lane16);   \
+        R1 = *(const uint4 *)(a_tile + ((size_t)(fa1 >> 1) * KB + (step) * 2 + (fa1 & 1)) * 1024 + lane16);   \
     } while (0)
 #define MLPL_LOAD_B(dst, step)                                                                                 \
     do {                                                                                                       \
@@ -113,10 +114,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                      \
                 dst[kb][j] = load_x8<WHOLE>(p, xr[j], (step) * kBK + 16 * kb + 8 * g);                                \
     } while (0)
-#define MLPL_STORE_A(buf)                                                                                      \
+#define MLPL_STORE_A(R0, R1, buf)                                                                              \
     do {                                                                                                       \
-        *(uint4 *)(lds_a[buf] + tid * 16) = ra0;                                                               \
-        *(uint4 *)(lds_a[buf] + (tid + kThreads) * 16) = ra1;                                                  \
+        *(uint4 *)(lds_a[buf] + tid * 16) = R0;                                                                \
+        *(uint4 *)(lds_a[buf] + (tid + kThreads) * 16) = R1;                                                   \
     } while (0)
 
     // Bias tiles of the four output tiles (the C operand of the first MFMA).
@@ -139,45 +140,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 
     // One K step: multiply with CUR (this step's B fragments) and the LDS tile `buf`.  A step with a
-    // successor first requests the next step's weights and rows (rows into NXT) and ends by storing
-    // those weights into the other LDS tile.  The K loop alternates the two B buffers and has no
-    // branch inside, so no fragment is copied and each row load is first waited for where it is used.
-    // Scheduling barriers hold the loads at the top of the step and the LDS store at its end:
-    // otherwise the compiler moves them next to each other and the store waits a full round trip.
+    // successor first requests the next step's rows (into NXT) and, with two successors, the weights
+    // two steps ahead (into the staging set RL, stored a step ago); it ends by storing the next step's
+    // weights (RS, requested a step ago) into the other LDS tile.  The K loop alternates the B buffers
+    // and the staging sets and has no branch inside, so no fragment is copied and each load is first
+    // waited for where it is used.  Scheduling barriers hold the loads at the top of the step and the
+    // LDS store at its end: otherwise the compiler moves them next to each other and the store waits
+    // a full round trip.
 #define MLPL_MFMAS(step, CUR)                                                                                  \
     do {                                                                                                       \
         const int buf = (step) & 1;                                                                            \
+        h8 af[2][4];                                                                                           \
         _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                                       \
-        {                                                                                                      \
-            h8 af[4];                                                                                          \
             _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                      \
-                af[i] = *(const h8 *)(lds_a[buf] + ((i * 2 + kb) * 64 + lane) * 16);                           \
+                af[kb][i] = *(const h8 *)(lds_a[buf] + ((i * 2 + kb) * 64 + lane) * 16);                       \
+        /* all eight fragment reads in flight before the first MFMA: left to itself the compiler */          \
+        /* interleaves them in pairs, and each pair waits out the LDS latency */                                \
+        asm volatile("" ::"v"(af[0][0]), "v"(af[0][1]), "v"(af[0][2]), "v"(af[0][3]), "v"(af[1][0]),           \
+                     "v"(af[1][1]), "v"(af[1][2]), "v"(af[1][3]));                                             \
+        _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                                       \
             _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                      \
                 _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                  \
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], CUR[kb][j], acc[i][j], 0, 0, 0); \
-        }                                                                                                      \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kb][i], CUR[kb][j], acc[i][j], 0, 0, 0); \
     } while (0)
-#define MLPL_STEP(step, CUR, NXT)                                                                              \
+#define MLPL_STEP(step, CUR, NXT, RL0, RL1, RS0, RS1, LOADA)                                                   \
     do {                                                                                                       \
-        MLPL_LOAD_A((step) + 1);                                                                               \
+        if (LOADA)                                                                                             \
+            MLPL_LOAD_A(RL0, RL1, (step) + 2);                                                                 \
         MLPL_LOAD_B(NXT, (step) + 1);                                                                          \
         __builtin_amdgcn_sched_barrier(0);                                                                     \
         MLPL_MFMAS(step, CUR);                                                                                 \
         __builtin_amdgcn_sched_barrier(0);                                                                     \
-        MLPL_STORE_A(((step) & 1) ^ 1);                                                                        \
+        MLPL_STORE_A(RS0, RS1, ((step) & 1) ^ 1);                                                              \
         __syncthreads();                                                                                       \
     } while (0)
 
     // kin is a multiple of 64, so the number of steps is even (and at least 2).
-    MLPL_LOAD_A(0);
+    MLPL_LOAD_A(ra0, ra1, 0);
+    MLPL_LOAD_A(rb0, rb1, 1);
     MLPL_LOAD_B(bc, 0);
-    MLPL_STORE_A(0);
+    MLPL_STORE_A(ra0, ra1, 0);
     __syncthreads();
     for (int step = 0; step + 2 < steps; step += 2) {
-        MLPL_STEP(step, bc, bn);
-        MLPL_STEP(step + 1, bn, bc);
+        MLPL_STEP(step, bc, bn, ra0, ra1, rb0, rb1, true);
+        MLPL_STEP(step + 1, bn, bc, rb0, rb1, ra0, ra1, true);
     }
-    MLPL_STEP(steps - 2, bc, bn);
+    MLPL_STEP(steps - 2, bc, bn, ra0, ra1, rb0, rb1, false);
     MLPL_MFMAS(steps - 1, bn);
 
     // Epilogue: lane (g, n) holds, for row 64 wave + 32 j + n, outputs 32 mt + 8 q + 4 g + i.
