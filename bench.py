@@ -285,24 +285,28 @@ def measure_layered(torch, B, workloads) -> dict:
     return res
 
 
-def read_clocks() -> dict:
-    """Current SCLK / MCLK levels from the amdgpu driver's DPM tables in sysfs (the level marked with
-    '*'), read in this process with no helper program; best effort, since the clocks cannot be locked
-    here.  With several cards visible, the first one that has the tables is read."""
-    import glob
+def current_dpm_level(text: str):
+    """The line the amdgpu driver marks with '*' in a pp_dpm_* table ("1: 2400Mhz *"; the level is a
+    number, or "S" for deep sleep), as {"level", "freq"}; None if no line is marked."""
+    for line in text.splitlines():
+        if line.rstrip().endswith("*") and ":" in line:
+            level, freq = line.split(":", 1)
+            return {"level": level.strip(), "freq": freq.replace("*", "").strip()}
+    return None
 
-    def current(path):
-        for line in Path(path).read_text().splitlines():
-            if line.rstrip().endswith("*"):
-                level, freq = line.split(":", 1)
-                return {"level": int(level), "freq": freq.replace("*", "").strip()}
-        return None
+
+def read_clocks() -> dict:
+    """Current SCLK / MCLK levels from the amdgpu driver's DPM tables in sysfs, read in this process
+    with no helper program; best effort, since the clocks cannot be locked here.  With several cards
+    visible, the first one that has the tables is read."""
+    import glob
 
     try:
         for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
             if os.path.exists(dev + "/pp_dpm_sclk"):
-                return {"card": dev.split("/")[-2], "sclk": current(dev + "/pp_dpm_sclk"),
-                        "mclk": current(dev + "/pp_dpm_mclk") if os.path.exists(dev + "/pp_dpm_mclk") else None}
+                mclk = dev + "/pp_dpm_mclk"
+                return {"card": dev.split("/")[-2], "sclk": current_dpm_level(Path(dev + "/pp_dpm_sclk").read_text()),
+                        "mclk": current_dpm_level(Path(mclk).read_text()) if os.path.exists(mclk) else None}
         return {"error": "no amdgpu DPM tables under /sys/class/drm"}
     except (OSError, ValueError) as e:
         return {"error": "%s: %s" % (type(e).__name__, str(e)[:200])}

@@ -57,3 +57,10 @@ def test_layered_workload_refuses_the_row_major_layout():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "packed layout" in r.stderr
+
+
+def test_clock_level_parser():
+    assert bench.current_dpm_level("0: 500Mhz\n1: 2400Mhz *\n") == {"level": "1", "freq": "2400Mhz"}
+    assert bench.current_dpm_level("S: 19Mhz *\n0: 500Mhz\n1: 2400Mhz\n") == {"level": "S", "freq": "19Mhz"}
+    assert bench.current_dpm_level("0: 500Mhz\n1: 2400Mhz\n") is None
+    assert "error" in bench.read_clocks() or "sclk" in bench.read_clocks()
