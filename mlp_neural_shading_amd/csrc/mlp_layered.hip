@@ -18,8 +18,8 @@
 //     never stored, and each output row depends on its own input row only;
 //   - the weights are shared by the four waves through a double-buffered LDS tile, K advancing 32 at
 //     a time: each step's tile is requested two steps ahead into one of two sets of staging
-//     registers and stored into LDS at the end of the step before it is used;
-//     the weight image is fragment-ordered per layer (natural K order: slot (kb, g, j) = feature
+//     registers and stored into LDS at the end of the step before it is used; the weight image is
+//     fragment-ordered per layer (natural K order: slot (kb, g, j) = feature
 //     16 kb + 8 g + j), so a fragment is one 16-byte LDS read per lane;
 //   - the bias is the C operand of the first MFMA of each output tile; the epilogue converts FP32 ->
 //     FP16 (nearest even), applies the leaky ReLU on packed FP16 and stores 4 outputs per lane.
@@ -99,8 +99,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 
     // Named registers rather than arrays indexed in helper lambdas: the compiler placed those in
-    // scratch memory.  The weight loads are issued before the row loads, so the LDS store of the
-    // weights waits for them alone.
+    // scratch memory.
     uint4 ra0, ra1, rb0, rb1;  // weight staging of the even (ra) and the odd (rb) K steps
     h8 bc[2][2], bn[2][2];  // [kb][j]: B fragments of the even and the odd K steps
 #define MLPL_LOAD_A(R0, R1, step)                                                                              \
@@ -112,7 +111,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     do {                                                                                                       \
         _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                                       \
             _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                      \
-                dst[kb][j] = load_x8<WHOLE>(p, xr[j], (step) * kBK + 16 * kb + 8 * g);                                \
+                dst[kb][j] = load_x8<WHOLE>(p, xr[j], (step) * kBK + 16 * kb + 8 * g);                         \
     } while (0)
 #define MLPL_STORE_A(R0, R1, buf)                                                                              \
     do {                                                                                                       \
