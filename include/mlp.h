@@ -78,7 +78,7 @@ int mlp_packed_size(int n_layers, const int32_t *widths, int layout, size_t *out
 /* The widths the selected kernel computes with (input width padded as the kernel reads it, every
  * layer width padded to its tile multiple): kernel_widths receives n_layers + 1 entries.  Shapes
  * without a dedicated kernel but within the fused limits run on a generic fused kernel whose widths
- * are all MLP_FUSED_MAX_WIDTH, zero-padded; wider or deeper shapes run layer by layer with the input
+ * are all 64 (when every width is at most 64) or all MLP_FUSED_MAX_WIDTH, zero-padded; wider or deeper shapes run layer by layer with the input
  * width padded to a multiple of 64 and every layer width to a multiple of 128.
  * Host only; no HIP call. */
 int mlp_plan_widths(int n_layers, const int32_t *widths, int layout, int32_t *kernel_widths);

@@ -136,8 +136,9 @@ int check_act(int act)
 }
 
 // The instance that serves (shape, layout, act): an exact-shape instance, else for the packed
-// layout with the vector activation and widths within the fused limits the generic instance for
-// that layer count, else none.
+// layout with the vector activation and widths within the fused limits the first generic instance
+// for that layer count whose padded widths cover the shape (the registry lists the 64-wide family
+// before the 128-wide one), else none.
 const KernelEntry *select(int n_layers, const int32_t *widths, int layout, int act)
 {
     int count = 0;
@@ -162,9 +163,15 @@ const KernelEntry *select(int n_layers, const int32_t *widths, int layout, int a
     for (int k = 0; k <= n_layers; ++k)
         if (widths[k] > MLP_FUSED_MAX_WIDTH)
             return nullptr;  // beyond the generic kernels
-    for (int i = 0; i < count; ++i)
-        if (all[i].generic && all[i].n_layers == n_layers)
+    for (int i = 0; i < count; ++i) {
+        if (!all[i].generic || all[i].n_layers != n_layers)
+            continue;
+        bool covers = true;
+        for (int k = 0; k <= n_layers; ++k)
+            covers &= widths[k] <= all[i].widths[k];
+        if (covers)
             return &all[i];
+    }
     return nullptr;
 }
 

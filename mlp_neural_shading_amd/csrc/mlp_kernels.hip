@@ -707,12 +707,16 @@ using NetStream = Net<64, 64, 64, 64, 64, 64, 64, 64, 16>;
         entry<NET, NT, WAVES, EU, LDS, kRowMajor, kVector, false>("mlp_fused<" TAG ",rowmajor,vector>"),          \
         entry<NET, NT, WAVES, EU, LDS, kRowMajor, kScalarised, false>("mlp_fused<" TAG ",rowmajor,scalarised>")
 
+#define MLP_GENERIC64(...) entry<Net<__VA_ARGS__>, 2, 8, 2, true, kPacked, kVector, true>
 #define MLP_GENERIC(...) entry<Net<__VA_ARGS__>, 1, 4, 1, false, kPacked, kVector, true>
 
 // Launch shapes, measured on MI355X: three waves per SIMD (12 per workgroup, one workgroup per compute
 // unit) beat two by 2-3 % on the 64-wide nets, whose kernels fit the 168-register budget without
 // spills; the net with a 128-wide layer needs more registers and stays at two (at three it spills and
 // runs ~15 % slower).  Tiles of 96 rows (NT = 3) were 1 % slower than 64 on the page-shaped net.
+// The generic kernels come in two families, every width padded to 64 (the image in LDS, two waves per
+// SIMD: at three the per-element input and output code spills 228-284 bytes) or to 128; a shape
+// takes the first family that covers it.
 static const KernelEntry kEntries[] = {
     // (net, 32-row tiles per wave, waves per workgroup, waves per SIMD, image in LDS)
     MLP_VARIANTS(NetSmall, 2, 8, 4, true, "16-32x7-4"),
@@ -720,6 +724,14 @@ static const KernelEntry kEntries[] = {
     MLP_VARIANTS(NetHetero, 2, 8, 2, true, "32-64-64-64-128-64-64-32-4"),
     MLP_VARIANTS(NetWide, 2, 8, 2, false, "64-128x7-4"),
     MLP_VARIANTS(NetStream, 2, 12, 3, true, "64-64x7-16"),
+    MLP_GENERIC64(64, 64)("mlp_fused<generic64,L=1>"),
+    MLP_GENERIC64(64, 64, 64)("mlp_fused<generic64,L=2>"),
+    MLP_GENERIC64(64, 64, 64, 64)("mlp_fused<generic64,L=3>"),
+    MLP_GENERIC64(64, 64, 64, 64, 64)("mlp_fused<generic64,L=4>"),
+    MLP_GENERIC64(64, 64, 64, 64, 64, 64)("mlp_fused<generic64,L=5>"),
+    MLP_GENERIC64(64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64,L=6>"),
+    MLP_GENERIC64(64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64,L=7>"),
+    MLP_GENERIC64(64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64,L=8>"),
     MLP_GENERIC(128, 128)("mlp_fused<generic128,L=1>"),
     MLP_GENERIC(128, 128, 128)("mlp_fused<generic128,L=2>"),
     MLP_GENERIC(128, 128, 128, 128)("mlp_fused<generic128,L=3>"),

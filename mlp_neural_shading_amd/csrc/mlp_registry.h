@@ -23,7 +23,7 @@ struct LaunchArgs {
 struct KernelEntry {
     const char *name;
     int n_layers;
-    int widths[9];      // exact instance: the widths it serves; generic: all 128 (any shape <= 128)
+    int widths[9];      // exact instance: the widths it serves; generic: all 64 or all 128 (any shape within)
     bool generic;
     int layout;
     int act;

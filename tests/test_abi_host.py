@@ -118,7 +118,8 @@ def test_plan_widths():
     assert B.mlp_plan_widths(workloads.get("small").widths) == [16, 32, 32, 32, 32, 32, 32, 32, 32]
     assert B.mlp_plan_widths(workloads.get("page").widths) == [32] + [64] * 7 + [32]
     assert B.mlp_plan_widths(workloads.get("hetero").widths) == [32, 64, 64, 64, 128, 64, 64, 32, 32]
-    assert B.mlp_plan_widths([2, 2, 1]) == [128, 128, 128]  # generic kernel, zero-padded
+    assert B.mlp_plan_widths([2, 2, 1]) == [64, 64, 64]  # generic kernel, zero-padded to 64
+    assert B.mlp_plan_widths([2, 65, 1]) == [128, 128, 128]  # a width above 64: the 128-wide family
     assert B.mlp_plan_widths([100, 300, 129, 7]) == [128, 384, 256, 128]  # layer by layer
     assert B.mlp_plan_widths([16] * 10) == [64] + [128] * 9
 
@@ -206,10 +207,10 @@ def _unpack(image, kw, widths):
     return Ws, bs
 
 
-@pytest.mark.parametrize("name", list(workloads.WORKLOADS) + ["generic-5-7-3"])
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS) + ["generic-5-7-3", "generic-100-30-7"])
 def test_packed_image_layout(name):
     if name.startswith("generic"):
-        widths = (5, 7, 3)
+        widths = tuple(int(w) for w in name.split("-")[1:])
         Ws, bs = workloads.init_weights(widths, seed=3)
     else:
         widths = workloads.WORKLOADS[name].widths

@@ -55,13 +55,14 @@ def test_sign_alternating_diagonal_net():
     assert np.array_equal(y, np.repeat(want[:, None], 4, axis=1))
 
 
-@pytest.mark.parametrize("seed", range(8))
-def test_integer_exact_nets_generic(oracle_mod, seed):
-    """Random non-square shapes (generic kernel): small non-negative integers, every intermediate
-    <= 2048, so the GPU must equal the oracle and the int64 product bit for bit."""
+@pytest.mark.parametrize("seed,hi", [(s, 129) for s in range(8)] + [(s, 65) for s in range(8, 12)])
+def test_integer_exact_nets_generic(oracle_mod, seed, hi):
+    """Random non-square shapes (generic kernels; widths below `hi`, so the last seeds run the
+    64-wide family): small non-negative integers, every intermediate <= 2048, so the GPU must equal
+    the oracle and the int64 product bit for bit."""
     rng = np.random.default_rng(200 + seed)
     L = int(rng.integers(1, 9))
-    widths = [int(w) for w in rng.integers(1, 129, size=L + 1)]
+    widths = [int(w) for w in rng.integers(1, hi, size=L + 1)]
     W = [np.zeros((widths[l + 1], widths[l]), np.int64) for l in range(L)]
     for l in range(L):
         for r in range(widths[l + 1]):
@@ -97,14 +98,17 @@ def _permutation_chain(widths, rng, diag=(1, -64, -1, -64, -1, -64, -1, 1)):
     return Ws, bs
 
 
-@pytest.mark.parametrize("name", DEDICATED + ["generic"])
+GENERIC_SHAPES = {"generic": (24, 40, 16, 72, 8, 100, 12, 56, 6), "generic64": (24, 40, 16, 48, 8, 60, 12, 56, 6)}
+
+
+@pytest.mark.parametrize("name", DEDICATED + ["generic", "generic64"])
 def test_permutation_chain_bit_exact(oracle_mod, name):
     rng = np.random.default_rng(31)
-    widths = workloads.get(name).widths if name != "generic" else (24, 40, 16, 72, 8, 100, 12, 56, 6)
+    widths = GENERIC_SHAPES[name] if name in GENERIC_SHAPES else workloads.get(name).widths
     Ws, bs = _permutation_chain(widths, rng)
     x = f16(rng.uniform(-1, 1, size=(1000 + 13, widths[0]))).view(np.uint16)
     ref = oracle_mod.mlp_forward(Ws, bs, x)
-    variants = VARIANTS if name != "generic" else VARIANTS[:1]
+    variants = VARIANTS[:1] if name in GENERIC_SHAPES else VARIANTS
     for v in variants:
         log("permutation chain", name, VNAME[v])
         y = run(Ws, bs, x, *v)
@@ -148,6 +152,22 @@ def test_subnormal_results_bit_exact(oracle_mod):
     Wg = [f16(np.pad(Ws[0].astype(np.float64), ((0, 0), (0, 1))))] + Ws[1:]
     xg = np.pad(x, ((0, 0), (0, 1)))
     assert np.array_equal(run(Wg, bs, xg), oracle_mod.mlp_forward(Wg, bs, xg))
+
+
+@pytest.mark.parametrize("widths,family", [
+    (GENERIC_SHAPES["generic64"], "generic64"), (GENERIC_SHAPES["generic"], "generic128"),
+    ((9, 64, 3), "generic64"), ((9, 65, 3), "generic128"), ((64,) * 9, "generic64")])
+def test_generic_families_random_weights(oracle_mod, widths, family):
+    """A shape with no dedicated kernel runs on the first generic family that covers it (every width
+    padded to 64, else to 128); random weights against the oracle at a ragged batch."""
+    rng = np.random.default_rng(len(widths) * 100 + widths[1])
+    Ws, bs = workloads.init_weights(widths, seed=5)
+    x = f16(rng.uniform(-1, 1, size=(4096 + 37, widths[0]))).view(np.uint16)
+    y = run(Ws, bs, x)
+    name = B.mlp_kernel_name(B.MLP_ACT_VECTOR)
+    log("generic shape", widths, name)
+    assert "<%s," % family in name, name
+    compare(y, oracle_mod.mlp_forward(Ws, bs, x, threads=host_threads()), what=str(widths))
 
 
 # ---- random-weight workloads at test sizes ---------------------------------------------------
