@@ -78,8 +78,9 @@ int mlp_packed_size(int n_layers, const int32_t *widths, int layout, size_t *out
 /* The widths the selected kernel computes with (input width padded as the kernel reads it, every
  * layer width padded to its tile multiple): kernel_widths receives n_layers + 1 entries.  Shapes
  * without a dedicated kernel but within the fused limits run on a generic fused kernel whose widths
- * are all 64 (when every width is at most 64) or all MLP_FUSED_MAX_WIDTH, zero-padded; wider or deeper shapes run layer by layer with the input
- * width padded to a multiple of 64 and every layer width to a multiple of 128.
+ * are all 64 (when every width is at most 64) or all MLP_FUSED_MAX_WIDTH, zero-padded; wider or
+ * deeper shapes run layer by layer with the input width padded to a multiple of 64 and every layer
+ * width to a multiple of 128.
  * Host only; no HIP call. */
 int mlp_plan_widths(int n_layers, const int32_t *widths, int layout, int32_t *kernel_widths);
 
@@ -125,10 +126,10 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
  * Asynchronous: the buffers must stay valid until the stream's work completes.  A network beyond the
  * fused limits runs as one kernel per layer over blocks of rows (as many as make the scratch below
  * 512 MiB, at least 65,536), its intermediate activations in two scratch buffers (block rows x the
- * widest hidden width, padded to 64, FP16) that the call
- * allocates and frees in order on `stream` from a memory pool the library keeps (so calls on
- * different streams never share them); MLP_ERR_OUT_OF_MEMORY if they cannot be allocated.  Must be called
- * with the device that was current at pack time.  Uses the activation form set by
+ * widest hidden width, padded to 64, FP16) that the call allocates and frees in order on `stream`
+ * from a memory pool the library keeps (so calls on different streams never share them);
+ * MLP_ERR_OUT_OF_MEMORY if they cannot be allocated.  Must be called with the device that was
+ * current at pack time.  Uses the activation form set by
  * mlp_set_activation_mode (default MLP_ACT_VECTOR).  Concurrent calls on different streams are
  * safe (the weights are read-only).  A device fault, should one occur, surfaces at the caller's
  * next synchronisation, as with any HIP kernel.
