@@ -137,8 +137,9 @@ int check_act(int act)
 
 // The instance that serves (shape, layout, act): an exact-shape instance, else for the packed
 // layout with the vector activation and widths within the fused limits the first generic instance
-// for that layer count whose padded widths cover the shape (the registry lists the 64-wide family
-// before the 128-wide one), else none.
+// for that layer count that serves the shape: padded widths that cover it and, for the vector-I/O
+// family, an input width that is a multiple of 8 and an output width that is a multiple of 4 (the
+// registry lists the 64-wide families before the 128-wide one), else none.
 const KernelEntry *select(int n_layers, const int32_t *widths, int layout, int act)
 {
     int count = 0;
@@ -169,6 +170,8 @@ const KernelEntry *select(int n_layers, const int32_t *widths, int layout, int a
         bool covers = true;
         for (int k = 0; k <= n_layers; ++k)
             covers &= widths[k] <= all[i].widths[k];
+        if (all[i].vec_io && (widths[0] % 8 != 0 || widths[n_layers] % 4 != 0))
+            covers = false;  // its vector loads and stores need these widths
         if (covers)
             return &all[i];
     }

@@ -130,12 +130,24 @@ struct Net {
     }
 };
 
+// A generic network whose caller widths are taken at run time but are known to allow vector input
+// and output (input width a multiple of 8, output width a multiple of 4): the host selects it only
+// for such shapes.
+template <int... W>
+struct VecNet : Net<W...> {};
+template <class N>
+struct runtime_vec_io : std::false_type {};
+template <int... W>
+struct runtime_vec_io<VecNet<W...>> : std::true_type {};
+
 template <class N, int NT, int LAYOUT, int ACT, bool GENERIC, bool LDS_W, class Src, bool DEFER>
 struct Body {
     static constexpr int L = N::L;
-    // Caller widths known at compile time (exact instances) allow vector loads and stores.
-    static constexpr bool kVecIn = !GENERIC && N::w[0] % 8 == 0;
-    static constexpr bool kVecOut = !GENERIC && N::w[L] % 4 == 0;
+    // Vector loads and stores: caller widths known at compile time (exact instances) that allow
+    // them, or a generic instance for vector-friendly widths (then the row strides are run time).
+    static constexpr bool kRtVec = GENERIC && runtime_vec_io<N>::value;
+    static constexpr bool kVecIn = (!GENERIC && N::w[0] % 8 == 0) || kRtVec;
+    static constexpr bool kVecOut = (!GENERIC && N::w[L] % 4 == 0) || kRtVec;
     // The last layer's outputs are held in registers and stored at the top of the next tile, after
     // that tile's inputs have been waited for: a store issued at the end of a tile would otherwise
     // sit in front of the next tile's wait (the vector-memory counter counts stores too) and every
@@ -143,7 +155,7 @@ struct Body {
     // waves share a SIMD and the weights come from LDS (measured: -2.8 % on the net with a 128-wide
     // layer; +0.4 % on the page net; +5 % on the net whose weights are read with buffer loads, where
     // the held store would sit in front of every weight fetch instead), so the instance chooses.
-    static constexpr bool kDefer = DEFER && kVecOut && N::MT(L - 1) == 1;
+    static constexpr bool kDefer = DEFER && !GENERIC && kVecOut && N::MT(L - 1) == 1;
     static constexpr int kQ = (N::w[L] + 7) / 8;  // 8-output groups holding real outputs
     struct Pending {
         h4 v[NT][kQ];
@@ -368,7 +380,7 @@ struct Body {
         for (int kb = 0; kb < KB0; ++kb) {
             const int c = 16 * kb + 8 * g;
             if constexpr (kVecIn) {
-                constexpr int w0 = N::w[0];
+                const int w0 = kRtVec ? a.w0 : N::w[0];  // a constant for exact instances
                 const int cc = (16 * kb + 16 <= w0 || c < w0) ? c : w0 - 8;  // folds for whole blocks
                 const char *base = (const char *)((const _Float16 *)a.x + row0 * w0);
                 R[kb][t] = *(const h8 *)(base + (unsigned)((r32 * w0 + cc) * 2));
@@ -400,7 +412,7 @@ struct Body {
         for (int kb = 0; kb < KB0; ++kb) {
             const int c = 16 * kb + 8 * g;
             if constexpr (kVecIn) {
-                constexpr int w0 = N::w[0];
+                const int w0 = kRtVec ? a.w0 : N::w[0];
                 const bool in = 16 * kb + 16 <= w0 || c < w0;  // folds for whole blocks
                 B[kb][t] = (live && in) ? R[kb][t] : (h8)(_Float16)0;
             } else {
@@ -435,7 +447,7 @@ struct Body {
                 const int c = 32 * mt + 8 * q + 4 * g;  // first of the 4 outputs held by this lane
                 const f4 part = {acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
                 if constexpr (kVecOut) {
-                    constexpr int wl = N::w[L];
+                    const int wl = kRtVec ? a.wL : N::w[L];
                     if (32 * mt + 8 * q < wl && c < wl)
                         *(h4 *)((char *)((_Float16 *)a.y + row0 * wl) + (unsigned)(((32 * t + n) * wl + c) * 2)) =
                             __builtin_convertvector(part, h4);
@@ -639,7 +651,7 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
         // keeps them as per-tile reads, each reused across the NT sample tiles.
         asm volatile("" ::: "memory");
         h8 B0[KB0][NT];
-        constexpr bool kWholeBlocks = B::kVecIn && N::w[0] % 16 == 0;
+        constexpr bool kWholeBlocks = B::kVecIn && !B::kRtVec && N::w[0] % 16 == 0;
         if (kWholeBlocks && (tile + 1) * kRows <= a.batch) {  // whole tile, whole blocks: no masking
 #pragma unroll
             for (int kb = 0; kb < KB0; ++kb)
@@ -690,6 +702,7 @@ KernelEntry entry(const char *name)
     e.weights_in_lds = LDS_W;
     e.launch = &launch<N, NT, WAVES, EU, LDS_W, LAYOUT, ACT, GENERIC>;
     e.func = (const void *)&mlp_fused<N, NT, WAVES, EU, LDS_W, LAYOUT, ACT, GENERIC>;
+    e.vec_io = GENERIC && runtime_vec_io<N>::value;
     return e;
 }
 
@@ -707,6 +720,7 @@ using NetStream = Net<64, 64, 64, 64, 64, 64, 64, 64, 16>;
         entry<NET, NT, WAVES, EU, LDS, kRowMajor, kVector, false>("mlp_fused<" TAG ",rowmajor,vector>"),          \
         entry<NET, NT, WAVES, EU, LDS, kRowMajor, kScalarised, false>("mlp_fused<" TAG ",rowmajor,scalarised>")
 
+#define MLP_GENERIC64V(...) entry<VecNet<__VA_ARGS__>, 2, 8, 2, true, kPacked, kVector, true>
 #define MLP_GENERIC64(...) entry<Net<__VA_ARGS__>, 2, 8, 2, true, kPacked, kVector, true>
 #define MLP_GENERIC(...) entry<Net<__VA_ARGS__>, 1, 4, 1, false, kPacked, kVector, true>
 
@@ -714,9 +728,11 @@ using NetStream = Net<64, 64, 64, 64, 64, 64, 64, 64, 16>;
 // unit) beat two by 2-3 % on the 64-wide nets, whose kernels fit the 168-register budget without
 // spills; the net with a 128-wide layer needs more registers and stays at two (at three it spills and
 // runs ~15 % slower).  Tiles of 96 rows (NT = 3) were 1 % slower than 64 on the page-shaped net.
-// The generic kernels come in two families, every width padded to 64 (the image in LDS, two waves per
-// SIMD: at three the per-element input and output code spills 228-284 bytes) or to 128; a shape
-// takes the first family that covers it.
+// The generic kernels come in three families: every width padded to 64 (the image in LDS, two waves
+// per SIMD: at three the per-element input and output code spills 228-284 bytes), with vector input
+// and output for input widths that are multiples of 8 and output widths that are multiples of 4 or
+// element by element for the others, and every width padded to 128; a shape takes the first family
+// that serves it.
 static const KernelEntry kEntries[] = {
     // (net, 32-row tiles per wave, waves per workgroup, waves per SIMD, image in LDS)
     MLP_VARIANTS(NetSmall, 2, 8, 4, true, "16-32x7-4"),
@@ -724,6 +740,14 @@ static const KernelEntry kEntries[] = {
     MLP_VARIANTS(NetHetero, 2, 8, 2, true, "32-64-64-64-128-64-64-32-4"),
     MLP_VARIANTS(NetWide, 2, 8, 2, false, "64-128x7-4"),
     MLP_VARIANTS(NetStream, 2, 12, 3, true, "64-64x7-16"),
+    MLP_GENERIC64V(64, 64)("mlp_fused<generic64v,L=1>"),
+    MLP_GENERIC64V(64, 64, 64)("mlp_fused<generic64v,L=2>"),
+    MLP_GENERIC64V(64, 64, 64, 64)("mlp_fused<generic64v,L=3>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64)("mlp_fused<generic64v,L=4>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=5>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=6>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=7>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=8>"),
     MLP_GENERIC64(64, 64)("mlp_fused<generic64,L=1>"),
     MLP_GENERIC64(64, 64, 64)("mlp_fused<generic64,L=2>"),
     MLP_GENERIC64(64, 64, 64, 64)("mlp_fused<generic64,L=3>"),

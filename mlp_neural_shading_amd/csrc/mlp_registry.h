@@ -32,6 +32,7 @@ struct KernelEntry {
     bool weights_in_lds;
     hipError_t (*launch)(const LaunchArgs &, int grid, hipStream_t);
     const void *func;   // kernel symbol, for occupancy queries
+    bool vec_io;        // generic instance with vector I/O: input width % 8 == 0, output width % 4 == 0 only
 };
 
 // All compiled instances: the FP16 kernels and the FP8 ones.
