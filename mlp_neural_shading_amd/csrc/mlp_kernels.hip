@@ -722,17 +722,17 @@ using NetStream = Net<64, 64, 64, 64, 64, 64, 64, 64, 16>;
 
 #define MLP_GENERIC64V(...) entry<VecNet<__VA_ARGS__>, 2, 8, 2, true, kPacked, kVector, true>
 #define MLP_GENERIC64(...) entry<Net<__VA_ARGS__>, 2, 8, 2, true, kPacked, kVector, true>
+#define MLP_GENERIC128V(...) entry<VecNet<__VA_ARGS__>, 1, 4, 1, false, kPacked, kVector, true>
 #define MLP_GENERIC(...) entry<Net<__VA_ARGS__>, 1, 4, 1, false, kPacked, kVector, true>
 
 // Launch shapes, measured on MI355X: three waves per SIMD (12 per workgroup, one workgroup per compute
 // unit) beat two by 2-3 % on the 64-wide nets, whose kernels fit the 168-register budget without
 // spills; the net with a 128-wide layer needs more registers and stays at two (at three it spills and
 // runs ~15 % slower).  Tiles of 96 rows (NT = 3) were 1 % slower than 64 on the page-shaped net.
-// The generic kernels come in three families: every width padded to 64 (the image in LDS, two waves
-// per SIMD: at three the per-element input and output code spills 228-284 bytes), with vector input
-// and output for input widths that are multiples of 8 and output widths that are multiples of 4 or
-// element by element for the others, and every width padded to 128; a shape takes the first family
-// that serves it.
+// The generic kernels pad every width to 64 (the image in LDS, two waves per SIMD: at three the
+// per-element input and output code spills 228-284 bytes) or to 128, each with vector input and
+// output for input widths that are multiples of 8 and output widths that are multiples of 4, or
+// element by element for the others; a shape takes the first family that serves it.
 static const KernelEntry kEntries[] = {
     // (net, 32-row tiles per wave, waves per workgroup, waves per SIMD, image in LDS)
     MLP_VARIANTS(NetSmall, 2, 8, 4, true, "16-32x7-4"),
@@ -756,6 +756,14 @@ static const KernelEntry kEntries[] = {
     MLP_GENERIC64(64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64,L=6>"),
     MLP_GENERIC64(64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64,L=7>"),
     MLP_GENERIC64(64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64,L=8>"),
+    MLP_GENERIC128V(128, 128)("mlp_fused<generic128v,L=1>"),
+    MLP_GENERIC128V(128, 128, 128)("mlp_fused<generic128v,L=2>"),
+    MLP_GENERIC128V(128, 128, 128, 128)("mlp_fused<generic128v,L=3>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128)("mlp_fused<generic128v,L=4>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=5>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=6>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=7>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=8>"),
     MLP_GENERIC(128, 128)("mlp_fused<generic128,L=1>"),
     MLP_GENERIC(128, 128, 128)("mlp_fused<generic128,L=2>"),
     MLP_GENERIC(128, 128, 128, 128)("mlp_fused<generic128,L=3>"),

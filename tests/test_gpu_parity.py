@@ -99,10 +99,10 @@ def _permutation_chain(widths, rng, diag=(1, -64, -1, -64, -1, -64, -1, 1)):
 
 
 GENERIC_SHAPES = {"generic": (24, 40, 16, 72, 8, 100, 12, 56, 6), "generic64": (24, 40, 16, 48, 8, 60, 12, 56, 6),
-                  "generic64v": (24, 40, 16, 48, 8, 60, 12, 56, 8)}
+                  "generic64v": (24, 40, 16, 48, 8, 60, 12, 56, 8), "generic128v": (24, 40, 16, 72, 8, 100, 12, 56, 8)}
 
 
-@pytest.mark.parametrize("name", DEDICATED + ["generic", "generic64", "generic64v"])
+@pytest.mark.parametrize("name", DEDICATED + ["generic", "generic64", "generic64v", "generic128v"])
 def test_permutation_chain_bit_exact(oracle_mod, name):
     rng = np.random.default_rng(31)
     widths = GENERIC_SHAPES[name] if name in GENERIC_SHAPES else workloads.get(name).widths
@@ -159,12 +159,13 @@ def test_subnormal_results_bit_exact(oracle_mod):
     (GENERIC_SHAPES["generic64"], "generic64"), (GENERIC_SHAPES["generic64v"], "generic64v"),
     (GENERIC_SHAPES["generic"], "generic128"), ((9, 64, 3), "generic64"), ((9, 65, 3), "generic128"),
     ((64,) * 9, "generic64v"), ((8, 64, 4), "generic64v"), ((48, 64, 64, 64, 64, 64, 8), "generic64v"),
-    ((40, 64, 6), "generic64")])
+    ((40, 64, 6), "generic64"), ((24, 40, 16, 72, 8, 100, 12, 56, 8), "generic128v"), ((64, 128, 4), "generic128v"),
+    ((128,) * 9, "generic128v"), ((72, 96, 6), "generic128")])
 def test_generic_families_random_weights(oracle_mod, widths, family):
     """A shape with no dedicated kernel runs on the first generic family that serves it (every width
-    padded to 64, with vector I/O when the input width is a multiple of 8 and the output width a
-    multiple of 4, else element by element; else every width padded to 128); random weights against
-    the oracle at a ragged batch."""
+    padded to 64, else to 128; each with vector I/O when the input width is a multiple of 8 and the
+    output width a multiple of 4, else element by element); random weights against the oracle at a
+    ragged batch."""
     rng = np.random.default_rng(len(widths) * 100 + widths[1])
     Ws, bs = workloads.init_weights(widths, seed=5)
     x = f16(rng.uniform(-1, 1, size=(4096 + 37, widths[0]))).view(np.uint16)
