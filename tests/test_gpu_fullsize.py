@@ -172,3 +172,33 @@ def test_boundary_errors_on_device():
     with pytest.raises(B.MlpError) as e:
         B.mlp_infer(4, x.data_ptr(), y.data_ptr())
     assert e.value.code == B.MLP_ERR_NOT_PACKED
+
+
+# Every kernel family evaluates a small or ragged batch exactly as it evaluates the same rows inside a
+# larger one: the tails (rows past the batch, masked loads and stores) must not change a bit.
+@pytest.mark.parametrize("widths", [
+    (64, 64, 64, 64, 64, 64, 64, 64, 16),   # dedicated (streaming shape)
+    (24, 40, 16, 48, 8, 60, 12, 56, 6),     # generic, 64-wide, element by element
+    (24, 40, 16, 48, 8, 60, 12, 56, 8),     # generic, 64-wide, vector I/O
+    (9, 65, 3),                             # generic, 128-wide, element by element
+    (24, 40, 16, 72, 8, 100, 12, 56, 8),    # generic, 128-wide, vector I/O
+    (64, 256, 256, 16),                     # layer by layer
+    (48,) * 13,                             # layer by layer, unaligned K
+])
+def test_batch_prefix_invariance_every_family(widths):
+    import torch
+
+    Ws, bs = workloads.init_weights(widths, seed=21)
+    rng = np.random.default_rng(22)
+    big = 4096 + 77
+    x = torch.from_numpy(rng.uniform(-1, 1, size=(big, widths[0])).astype(np.float16)).to("cuda")
+    B.mlp_pack_weights(Ws, bs)
+    log("prefix invariance", widths, B.mlp_kernel_name(B.MLP_ACT_VECTOR))
+    s = torch.cuda.current_stream().cuda_stream
+    full = torch.empty((big, widths[-1]), dtype=torch.float16, device="cuda")
+    B.mlp_infer(big, x.data_ptr(), full.data_ptr(), s)
+    for n in (1, 2, 31, 33, 63, 65, 257, 1000):
+        part = torch.full((n, widths[-1]), float("nan"), dtype=torch.float16, device="cuda")
+        B.mlp_infer(n, x.data_ptr(), part.data_ptr(), s)
+        torch.cuda.synchronize()
+        assert torch.equal(part, full[:n]), (widths, n)
