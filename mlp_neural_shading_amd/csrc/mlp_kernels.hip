@@ -610,15 +610,17 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
     int64_t next = lo + WAVES + wave;
 
     // The first tile's inputs are requested right behind the weight image's loads, so the two
-    // latencies overlap; every later tile's inputs are requested one tile ahead.
+    // latencies overlap; every later tile's inputs are requested at the end of the tile before it,
+    // straight into the layer-0 fragments (no prefetch buffer and no copy: 16 fewer registers; the
+    // other waves of the SIMD cover the wait).
     constexpr int KB0 = N::KB(0);  // a constant expression, so the loops below fully unroll
-    h8 Bnext[KB0][NT];
+    h8 B0[KB0][NT];  // this tile's inputs, loaded at the end of the previous tile
     Src src;
     if constexpr (LDS_W) {
         __shared__ __attribute__((aligned(16))) uint8_t lds[lbytes];
         constexpr int kChunks = (bytes + WAVES * 64 * 16 - 1) / (WAVES * 64 * 16);
         const auto chunks = stage_load<bytes, WAVES * 64>(a.image, std::make_integer_sequence<int, kChunks>());
-        B::load_inputs(Bnext, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
+        B::load_inputs(B0, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
         if constexpr (LAYOUT == kPacked)
             stage_store<bytes, WAVES * 64>(lds, chunks, std::make_integer_sequence<int, kChunks>());
         else
@@ -628,12 +630,12 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
         __shared__ __attribute__((aligned(16))) uint8_t lds[kSplit];
         constexpr int kChunks = (kSplit + WAVES * 64 * 16 - 1) / (WAVES * 64 * 16);
         const auto chunks = stage_load<kSplit, WAVES * 64>(a.image, std::make_integer_sequence<int, kChunks>());
-        B::load_inputs(Bnext, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
+        B::load_inputs(B0, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
         stage_store<kSplit, WAVES * 64>(lds, chunks, std::make_integer_sequence<int, kChunks>());
         src.base = lds;
         src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.image, 0, bytes, kBufferRsrcWord3);
     } else {
-        B::load_inputs(Bnext, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
+        B::load_inputs(B0, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
         src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.image, 0, bytes, kBufferRsrcWord3);
     }
     if (threadIdx.x == 0)
@@ -650,26 +652,18 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
         // read out of the tile loop and the whole image (up to ~1 KB per lane) spills.  The barrier
         // keeps them as per-tile reads, each reused across the NT sample tiles.
         asm volatile("" ::: "memory");
-        h8 B0[KB0][NT];
         constexpr bool kWholeBlocks = B::kVecIn && !B::kRtVec && N::w[0] % 16 == 0;
-        if (kWholeBlocks && (tile + 1) * kRows <= a.batch) {  // whole tile, whole blocks: no masking
-#pragma unroll
-            for (int kb = 0; kb < KB0; ++kb)
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    B0[kb][t] = Bnext[kb][t];
-        } else {
-            B::mask_inputs(B0, Bnext, a, tile * kRows, lane, std::make_integer_sequence<int, NT>());
-        }
+        if (!(kWholeBlocks && (tile + 1) * kRows <= a.batch))
+            B::mask_inputs(B0, B0, a, tile * kRows, lane, std::make_integer_sequence<int, NT>());
         if constexpr (B::kDefer)
             if (held_row0 >= 0)
                 B::store_pending(pend, a, held_row0, lane);
-        if (next < hi)
-            B::load_inputs(Bnext, a, next * kRows, lane, std::make_integer_sequence<int, NT>());
         const int64_t after = lo + __builtin_amdgcn_readfirstlane(claimed);  // claimed one tile ago
         if (lane == 0)
             claimed = atomicAdd(&next_tile, 1);
         B::template layer<0>(src, B0, a, tile * kRows, lane, pend);
+        if (next < hi)
+            B::load_inputs(B0, a, next * kRows, lane, std::make_integer_sequence<int, NT>());
         held_row0 = tile * kRows;
         tile = next;
         next = after;
