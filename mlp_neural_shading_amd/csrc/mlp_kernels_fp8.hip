@@ -368,12 +368,12 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
         asm volatile("" ::: "memory");
         i8 B0[KB0][NT];
         B::convert_inputs(B0, Rnext, a, tile * kRows, lane, std::make_integer_sequence<int, NT>());
-        if (next < hi)
-            B::load_inputs(Rnext, a, next * kRows, lane, std::make_integer_sequence<int, NT>());
         const int64_t after = lo + __builtin_amdgcn_readfirstlane(claimed);
         if (lane == 0)
             claimed = atomicAdd(&next_tile, 1);
         B::template layer<0>(lds, B0, a, tile * kRows, lane);
+        if (next < hi)
+            B::load_inputs(Rnext, a, next * kRows, lane, std::make_integer_sequence<int, NT>());
         tile = next;
         next = after;
     }
