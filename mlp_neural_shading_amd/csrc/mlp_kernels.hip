@@ -714,6 +714,7 @@ using NetStream = Net<64, 64, 64, 64, 64, 64, 64, 64, 16>;
         entry<NET, NT, WAVES, EU, LDS, kRowMajor, kVector, false>("mlp_fused<" TAG ",rowmajor,vector>"),          \
         entry<NET, NT, WAVES, EU, LDS, kRowMajor, kScalarised, false>("mlp_fused<" TAG ",rowmajor,scalarised>")
 
+#define MLP_GENERIC64V3(...) entry<VecNet<__VA_ARGS__>, 2, 12, 3, true, kPacked, kVector, true>
 #define MLP_GENERIC64V(...) entry<VecNet<__VA_ARGS__>, 2, 8, 2, true, kPacked, kVector, true>
 #define MLP_GENERIC64(...) entry<Net<__VA_ARGS__>, 2, 8, 2, true, kPacked, kVector, true>
 #define MLP_GENERIC128V(...) entry<VecNet<__VA_ARGS__>, 1, 8, 2, false, kPacked, kVector, true>
@@ -726,9 +727,11 @@ using NetStream = Net<64, 64, 64, 64, 64, 64, 64, 64, 16>;
 // The generic kernels pad every width to 64 (the image in LDS, two waves per SIMD: at three the
 // per-element input and output code spills 228-284 bytes) or to 128, each with vector input and
 // output for input widths that are multiples of 8 and output widths that are multiples of 4, or
-// element by element for the others; a shape takes the first family that serves it.  The 128-wide
-// vector kernels fit two waves per SIMD (169-218 registers; 4-23 % faster than one), the 128-wide
-// element-by-element ones spill there and stay at one.
+// element by element for the others; a shape takes the first family that serves it.  The 64-wide
+// vector kernels run at three waves per SIMD up to six layers (1-5 % faster than two; seven and eight
+// layers spill there and stay at two); the 128-wide vector kernels fit two waves per SIMD (169-218
+// registers; 4-23 % faster than one), the 128-wide element-by-element ones spill there and stay at
+// one.
 static const KernelEntry kEntries[] = {
     // (net, 32-row tiles per wave, waves per workgroup, waves per SIMD, image in LDS)
     MLP_VARIANTS(NetSmall, 2, 8, 4, true, "16-32x7-4"),
@@ -736,12 +739,12 @@ static const KernelEntry kEntries[] = {
     MLP_VARIANTS(NetHetero, 2, 8, 2, true, "32-64-64-64-128-64-64-32-4"),
     MLP_VARIANTS(NetWide, 2, 8, 2, false, "64-128x7-4"),
     MLP_VARIANTS(NetStream, 2, 12, 3, true, "64-64x7-16"),
-    MLP_GENERIC64V(64, 64)("mlp_fused<generic64v,L=1>"),
-    MLP_GENERIC64V(64, 64, 64)("mlp_fused<generic64v,L=2>"),
-    MLP_GENERIC64V(64, 64, 64, 64)("mlp_fused<generic64v,L=3>"),
-    MLP_GENERIC64V(64, 64, 64, 64, 64)("mlp_fused<generic64v,L=4>"),
-    MLP_GENERIC64V(64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=5>"),
-    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=6>"),
+    MLP_GENERIC64V3(64, 64)("mlp_fused<generic64v,L=1>"),
+    MLP_GENERIC64V3(64, 64, 64)("mlp_fused<generic64v,L=2>"),
+    MLP_GENERIC64V3(64, 64, 64, 64)("mlp_fused<generic64v,L=3>"),
+    MLP_GENERIC64V3(64, 64, 64, 64, 64)("mlp_fused<generic64v,L=4>"),
+    MLP_GENERIC64V3(64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=5>"),
+    MLP_GENERIC64V3(64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=6>"),
     MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=7>"),
     MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=8>"),
     MLP_GENERIC64(64, 64)("mlp_fused<generic64,L=1>"),
