@@ -65,11 +65,13 @@ enum {
 #define MLP_FUSED_MAX_LAYERS 8
 #define MLP_FUSED_MAX_WIDTH 128
 
-/* Size in bytes of the device image mlp_pack_weights would build for this shape and layout.
+/* Size in bytes of the device image mlp_pack_weights would build for this shape and layout: the
+ * size query that precedes the one-time conversion ("Row-major versus InferencingOptimal weights":
+ * the application asks for the converted matrix's size before converting into it).
  *   n_layers  number of affine layers, 1..MLP_MAX_LAYERS
  *   widths    n_layers + 1 entries: widths[0] = input width, widths[l] = output width of layer l,
  *             each 1..MLP_MAX_WIDTH
- *   layout    MLP_LAYOUT_ROW_MAJOR or MLP_LAYOUT_PACKED
+ *   layout    MLP_LAYOUT_ROW_MAJOR, MLP_LAYOUT_PACKED or MLP_LAYOUT_PACKED_FP8
  *   out_bytes receives the size
  * Host only; no HIP call.  MLP_ERR_UNSUPPORTED for a row-major request on a shape that no dedicated
  * kernel serves (generic fused shapes and layer-by-layer shapes take the packed layout only). */
@@ -105,6 +107,9 @@ int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const 
  * `stream` ("Row-major versus InferencingOptimal weights": the conversion can be recorded into the
  * GPU's command stream instead of run on the host).  The resulting device image is bit for bit the
  * one mlp_pack_weights builds, and it becomes the current network.
+ *   layout    MLP_LAYOUT_PACKED (every shape, fused or layer by layer) or MLP_LAYOUT_ROW_MAJOR (the
+ *             dedicated shapes); MLP_LAYOUT_PACKED_FP8 returns MLP_ERR_UNSUPPORTED before any HIP
+ *             call (its per-row scales and E4M3 rounding are written by the host packer only)
  *   d_weights n_layers host-memory entries, each a device pointer to [widths[l+1]][widths[l]] FP16
  *             row-major, 2-byte aligned
  *   d_biases  n_layers host-memory entries, each a device pointer to [widths[l+1]] FP16
@@ -117,7 +122,11 @@ int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const 
 int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *const *d_weights,
                             const void *const *d_biases, int layout, void *stream);
 
-/* Evaluate the current network on `batch` rows: enqueue one kernel on `stream` and return.
+/* Evaluate the current network on `batch` rows: enqueue one kernel on `stream` and return.  This is
+ * the timed inference pass of "Profiling neural material inference", section "Experiment setup" (one
+ * dispatch evaluates every row through every layer); per layer y = W h + b in FP32 from FP16
+ * operands, rounded to FP16, then max(v, v * half(0.01)) except after the last layer (section "Bad
+ * versus good activation").
  *   batch    number of rows, >= 0 (0: nothing is launched, returns MLP_OK)
  *   in_ptr   device pointer, [batch][widths[0]] FP16 row-major, 16-byte aligned
  *   out_ptr  device pointer, [batch][widths[n_layers]] FP16 row-major, 16-byte aligned, must not
@@ -152,7 +161,9 @@ int mlp_debug_read_packed(void *host_dst, size_t bytes);
 /* Message for the last error on the calling thread ("" if none).  Valid until the next call. */
 const char *mlp_last_error(void);
 
-/* Free the current device image and return the scratch memory the layer-by-layer path keeps cached
+/* Free the current device image (the converted matrices of "Row-major versus InferencingOptimal
+ * weights", which live until the weights change) and return the scratch memory the layer-by-layer
+ * path keeps cached
  * (its stream-ordered frees complete first).  Idempotent; mlp_infer then returns MLP_ERR_NOT_PACKED.
  * Not thread-safe with respect to mlp_pack_weights or an mlp_infer still being enqueued. */
 void mlp_release(void);

@@ -356,6 +356,10 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
         rc = check_weights(n_layers, (const uint16_t *const *)d_weights, (const uint16_t *const *)d_biases);
     if (rc != MLP_OK)
         return rc;
+    // The conversion kernel writes the FP16 images (packed and row-major) only.
+    if (layout == MLP_LAYOUT_PACKED_FP8)
+        return fail(MLP_ERR_UNSUPPORTED, "the device conversion writes the FP16 layouts only; pack the FP8 "
+                    "layout with mlp_pack_weights");
     for (int l = 0; l < n_layers; ++l)
         if (((uintptr_t)d_weights[l] | (uintptr_t)d_biases[l]) & 1)
             return fail(MLP_ERR_INVALID_ARGUMENT, "d_weights[%d] or d_biases[%d] is not 2-byte aligned", l, l);

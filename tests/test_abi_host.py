@@ -88,6 +88,23 @@ def test_device_pack_validation():
     assert L.mlp_pack_weights_device(2, w3.ctypes.data, two, two, B.MLP_LAYOUT_ROW_MAJOR, None) == B.MLP_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("name", ["small", "page", "hetero", "wide", "stream"])
+def test_device_pack_refuses_the_fp8_layout(name):
+    """The conversion kernel writes the FP16 images only: an FP8 request on a shape that has an FP8
+    kernel must come back UNSUPPORTED before any HIP call (here, with or without a GPU), and the
+    current network must stay as it was."""
+    L = B.lib()
+    wl = workloads.get(name)
+    w = np.asarray(wl.widths, np.int32)
+    n = len(w) - 1
+    assert B.mlp_packed_size(w, B.MLP_LAYOUT_PACKED_FP8) > 0  # the host packer serves it
+    ptrs = (ctypes.c_void_p * n)(*[0x10000 * (i + 1) for i in range(n)])
+    B.mlp_release()
+    assert L.mlp_pack_weights_device(n, w.ctypes.data, ptrs, ptrs, B.MLP_LAYOUT_PACKED_FP8, None) == B.MLP_ERR_UNSUPPORTED
+    assert "FP16 layouts only" in B.mlp_last_error()
+    assert _err(B.mlp_kernel_name, 0) == B.MLP_ERR_NOT_PACKED  # nothing was installed
+
+
 @pytest.mark.skipif(_have_gpu(), reason="checks the error path taken when no GPU is visible")
 def test_device_pack_without_a_device_reports_hip_error():
     with pytest.raises(B.MlpError) as e:
