@@ -78,7 +78,8 @@ enum {
 int mlp_packed_size(int n_layers, const int32_t *widths, int layout, size_t *out_bytes);
 
 /* The widths the selected kernel computes with (input width padded as the kernel reads it, every
- * layer width padded to its tile multiple): kernel_widths receives n_layers + 1 entries.  Shapes
+ * layer width padded to its tile multiple, except that a last layer of at most 4 outputs on a
+ * dedicated FP16 kernel is computed 4 wide): kernel_widths receives n_layers + 1 entries.  Shapes
  * without a dedicated kernel but within the fused limits run on a generic fused kernel whose widths
  * are all 64 (when every width is at most 64) or all MLP_FUSED_MAX_WIDTH, zero-padded; wider or
  * deeper shapes run layer by layer with the input width padded to a multiple of 64 and every layer

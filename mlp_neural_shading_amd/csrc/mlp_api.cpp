@@ -239,6 +239,8 @@ int mlp_plan_widths(int n_layers, const int32_t *widths, int layout, int32_t *ke
     kernel_widths[0] = mlpl::k0_pad(e->widths[0]);
     for (int l = 1; l <= n_layers; ++l)
         kernel_widths[l] = mlpl::round_up(e->widths[l], mlpl::kTileM);
+    if (layout != MLP_LAYOUT_PACKED_FP8 && mlpl::narrow_last(e->widths, n_layers))
+        kernel_widths[n_layers] = mlpl::kNarrowOut;  // the 16x16x32 form: 4 outputs per sample half
     return ok();
 }
 

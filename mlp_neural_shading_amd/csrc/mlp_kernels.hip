@@ -40,6 +40,7 @@ typedef float f16x __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ _Float16 slope() { return __builtin_bit_cast(_Float16, (unsigned short)0x211f); }
 
 __device__ __forceinline__ f16x mfma(h8 a, h8 b, f16x c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+__device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
 // Vector leaky ReLU on eight FP16 values: two packed instructions for every two values.
 __device__ __forceinline__ h8 leaky_vector(h8 v)
@@ -156,6 +157,8 @@ struct Body {
     // layer; +0.4 % on the page net; +5 % on the net whose weights are read with buffer loads, where
     // the held store would sit in front of every weight fetch instead), so the instance chooses.
     static constexpr bool kDefer = DEFER && !GENERIC && kVecOut && N::MT(L - 1) == 1;
+    // A last layer of at most 4 outputs runs on the 16x16x32 MFMA (mlp_layout.h, narrow_last).
+    static constexpr bool kNarrow = !GENERIC && mlpl::narrow_last(N::w, L);
     static constexpr int kQ = (N::w[L] + 7) / 8;  // 8-output groups holding real outputs
     struct Pending {
         h4 v[NT][kQ];
@@ -242,6 +245,104 @@ struct Body {
         }
     }
 
+    // ---- narrow last layer: both 16-sample halves of each B fragment in one 16x16x32 MFMA ---------
+    //
+    // Lane (a, i) of the A fragment holds output narrow_row(lane) over the slots of group lane / 32
+    // (zeros elsewhere), so rows 0..3 of the result are sample 32 t + c and rows 4..7 sample
+    // 32 t + 16 + c, and lane s < 32 ends with the four outputs of sample 32 t + s (mlp_layout.h).
+
+    template <int l>
+    static __device__ __forceinline__ h8 narrow_frag(const Src &src, int kb, int lane)
+    {
+        if constexpr (LAYOUT == kPacked) {
+            return ld16<l>(src, lane * 16, (int)mlpl::pk_a_off(N::w, l) + kb * mlpl::kFragBytes);
+        } else {
+            // gathered from the row-major matrix: row narrow_row(lane), the slot features of group g
+            constexpr int win = N::w[l], wout = N::w[l + 1];
+            static_assert(win % 8 == 0, "row-major layers need w_in % 8 == 0");
+            constexpr int stride = LDS_W ? mlpl::rml_stride(l, win) : win * 2;
+            constexpr int w_off = LDS_W ? (int)mlpl::rml_w_off(N::w, l) : (int)mlpl::rm_w_off(N::w, l);
+            const int g = lane >> 5, r = mlpl::narrow_row(lane);
+            const bool live = r >= 0 && r < wout;
+            const int m = live ? r : 0;
+            h8 a = (h8)(_Float16)0;
+            if constexpr (l == 0) {
+                if (live && 16 * kb + 8 * g < win)
+                    a = src.load16(m * stride + 8 * g * 2, w_off + 16 * kb * 2);
+            } else {
+                const int f0 = 16 * kb + 4 * g, f1 = f0 + 8;
+                h4 lo = (h4)(_Float16)0, hi = (h4)(_Float16)0;
+                if (live && f0 < win)
+                    lo = src.load8(m * stride + 4 * g * 2, w_off + 16 * kb * 2);
+                if (live && f1 < win)
+                    hi = src.load8(m * stride + 4 * g * 2, w_off + (16 * kb + 8) * 2);
+                a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            return a;
+        }
+    }
+
+    // C operand: b[0..3] in the lanes of both sample halves (a = lane / 16 < 2), zero in the others.
+    template <int l>
+    static __device__ __forceinline__ f4 narrow_bias(const Src &src, int lane)
+    {
+        if constexpr (LAYOUT == kPacked) {
+            return __builtin_bit_cast(f4, ld16<l>(src, (lane >> 4) * 16, (int)mlpl::pk_b_off(N::w, l)));
+        } else {
+            // b [w_out] FP16, its section zero-padded to 16 bytes
+            const int soff = LDS_W ? (int)mlpl::rml_b_off(N::w, l) : (int)mlpl::rm_b_off(N::w, l);
+            h4 q = src.load8(0, soff);
+            if (lane >= 32)
+                q = (h4)(_Float16)0;
+            return __builtin_convertvector(q, f4);
+        }
+    }
+
+    template <int l>
+    static __device__ __forceinline__ void narrow_layer(const Src &src, const h8 (&Bin)[N::KB(l)][NT],
+                                                        const LaunchArgs &a, int64_t row0, int lane, Pending &pend)
+    {
+        constexpr int KB = N::KB(l);
+        h8 af[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            af[kb] = narrow_frag<l>(src, kb, lane);
+        const f4 bias = narrow_bias<l>(src, lane);
+        f4 acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = mfma16(af[0], Bin[0][t], bias);
+#pragma unroll
+        for (int kb = 1; kb < KB; ++kb)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = mfma16(af[kb], Bin[kb][t], acc[t]);
+        if constexpr (kDefer) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                pend.v[t][0] = __builtin_convertvector(acc[t], h4);  // lanes < 32 hold real rows
+        } else {
+            constexpr int wl = N::w[L];
+            if (lane < 32) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int64_t row = row0 + 32 * t + lane;
+                    if (row < a.batch) {
+                        const h4 v = __builtin_convertvector(acc[t], h4);
+                        if constexpr (kVecOut) {
+                            *(h4 *)((char *)((_Float16 *)a.y + row0 * wl) + (unsigned)((32 * t + lane) * wl * 2)) = v;
+                        } else {
+                            _Float16 *yr = (_Float16 *)a.y + row * wl;
+#pragma unroll
+                            for (int i = 0; i < wl; ++i)
+                                yr[i] = v[i];
+                        }
+                    }
+                }
+            }
+        }
+    }
+
     // ---- one layer: NT sample tiles x MT output tiles x KB input blocks --------------------
     //
     // Software-pipelined over the output tiles mt: the fragments of tile mt+1 are requested first,
@@ -301,6 +402,10 @@ struct Body {
         // scheduler front-loads the whole network's fragments and runs out of registers.
         if constexpr (!LDS_W)
             asm volatile("" ::: "memory");
+        if constexpr (kNarrow && l == L - 1) {
+            narrow_layer<l>(wb, Bin, a, row0, lane, pend);
+            return;
+        }
         h8 af[KB];
         f16x bias;
         fetch<l>(wb, 0, af, bias, lane);

@@ -21,6 +21,7 @@
 // Packed image, per layer l (MT = output tiles of 32, KB = input blocks of 16):
 //   A fragments  [mt][kb][lane][8 halves]   1024 bytes per fragment, one ds_read_b128 per lane
 //   bias tiles   [mt][g][16 floats]         FP32, lane (g, n) reads b[32 mt + 8 q + 4 g + i]
+// (a last layer of at most 4 outputs is laid out for a smaller MFMA, see narrow_last below).
 // Row-major image, per layer l: W_l [w_out][w_in] FP16 as given, then b_l [w_out] FP16, each
 // section padded to a multiple of 16 bytes.
 #pragma once
@@ -49,6 +50,26 @@ constexpr int slot_feature(int l, int kb, int g, int j)
 
 // Output feature held in accumulator element j of lane group g for output tile mt.
 constexpr int acc_feature(int mt, int g, int j) { return kTileM * mt + 8 * (j / 4) + 4 * g + (j % 4); }
+
+// Narrow last layer (at most 4 outputs, e.g. the page network's 4-wide output).  A 32x32 tile would
+// spend 28 of its 32 rows on padding, so this layer runs as v_mfma_f32_16x16x32_f16 instead (half the
+// MFMA time per input block), which reads a lane of the 32-sample B fragment as it stands: lane
+// l = 16 a + c of that MFMA is column c and K group a, which here carries sample 32 t + 16 (a % 2) + c
+// and the slots of group a / 2.  The A fragment therefore holds every output twice, once per sample
+// half: lane (a, i) holds output i % 4 over the slots of group a / 2 when i / 4 == a % 2 and i < 8,
+// else zeros, so D rows 0..3 are the outputs of samples 32 t + c and rows 4..7 those of samples
+// 32 t + 16 + c.  By the MFMA's output layout (lane 16 a + c holds rows 4 a .. 4 a + 3 of column c),
+// lane s < 32 ends with the four outputs of sample 32 t + s.
+//   A fragments  [kb][lane][8 halves]     one per input block, slots as for any other layer
+//   bias         [a][4 floats]            b[0..3] for a = 0, 1 (the C operand of both halves), 0 for
+//                                         a = 2, 3; the rest of the layer's bias tile is zero
+constexpr int kNarrowOut = 4;
+constexpr bool narrow_last(const int *w, int L) { return w[L] <= kNarrowOut; }
+// Output (0..3) that lane `lane` of a narrow A fragment holds, or -1 for a zero lane.
+constexpr int narrow_row(int lane)
+{
+    return (lane % 16) < 2 * kNarrowOut && (lane % 16) / kNarrowOut == (lane / 16) % 2 ? (lane % 16) % kNarrowOut : -1;
+}
 
 constexpr size_t pk_a_bytes(const int *w, int l) { return (size_t)m_tiles(w, l) * k_blocks(w, l) * kFragBytes; }
 constexpr size_t pk_layer_bytes(const int *w, int l) { return pk_a_bytes(w, l) + (size_t)m_tiles(w, l) * kBiasTileBytes; }

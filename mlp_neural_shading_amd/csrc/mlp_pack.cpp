@@ -142,6 +142,23 @@ void pack_image(int n_layers, const int *widths, const int *kw, const uint16_t *
         }
         const int MT = mlpl::m_tiles(kw, l), KB = mlpl::k_blocks(kw, l);
         uint16_t *A = (uint16_t *)(dst + mlpl::pk_a_off(kw, l));
+        if (l == n_layers - 1 && mlpl::narrow_last(kw, n_layers)) {
+            // [kb][lane][8]: output narrow_row(lane) over the slots of group lane / 32, both sample halves
+            for (int kb = 0; kb < KB; ++kb)
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int r = mlpl::narrow_row(lane), g = lane / 32;
+                    uint16_t *frag = A + ((size_t)kb * 64 + lane) * 8;
+                    for (int j = 0; j < 8; ++j) {
+                        const int f = mlpl::slot_feature(l, kb, g, j);
+                        frag[j] = (r >= 0 && r < wout && f < win) ? W[(size_t)r * win + f] : 0;
+                    }
+                }
+            float *B = (float *)(dst + mlpl::pk_b_off(kw, l));
+            for (int a = 0; a < 2; ++a)
+                for (int r = 0; r < wout; ++r)
+                    B[4 * a + r] = half_bits_to_float(b[r]);
+            continue;
+        }
         for (int mt = 0; mt < MT; ++mt)
             for (int kb = 0; kb < KB; ++kb)
                 for (int lane = 0; lane < 64; ++lane) {

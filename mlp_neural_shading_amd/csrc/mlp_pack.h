@@ -25,6 +25,7 @@ struct PackArgs {
     const uint16_t *w[8];
     const uint16_t *b[8];
     int win[8], wout[8], mt[8], kb[8];
+    int narrow[8];  // 1: the narrow last-layer layout of mlp_layout.h (packed layout, one output tile)
     uint32_t a_off[8], b_off[8], first[8], items[8];
     int layout;
     int natural;  // 1: every layer in natural K order (the layered image), 0: the fused kernels' order

@@ -28,7 +28,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs p)
             if (i < p.first[l]) {  // A fragments [mt][kb][lane][8]
                 const int lane = (int)(i % 64), frag = (int)(i / 64);
                 const int kb = frag % p.kb[l], mt = frag / p.kb[l];
-                const int g = lane / 32, r = mlpl::kTileM * mt + lane % 32;
+                const int g = lane / 32;
+                // a narrow last layer has one tile whose lanes carry outputs 0..3 twice (or zeros)
+                const int nr = mlpl::narrow_row(lane);
+                const int r = p.narrow[l] ? (nr >= 0 ? nr : wout) : mlpl::kTileM * mt + lane % 32;
                 uint16_t v[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -41,7 +44,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs p)
                 float v[16];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const int r = mlpl::acc_feature(mt, g, j);
+                    // narrow: floats 0..3 and 4..7 of the tile are b[0..3], the rest zero
+                    const int r = p.narrow[l] ? (g == 0 && j < 8 ? j % 4 : wout) : mlpl::acc_feature(mt, g, j);
                     v[j] = r < wout ? (float)__builtin_bit_cast(_Float16, b[r]) : 0.0f;
                 }
                 float4 *d = (float4 *)(p.dst + p.b_off[l] + (size_t)(mt * 32 + g * 16) * 4);
@@ -72,6 +76,7 @@ void fill_pack_args(int n_layers, const int *widths, const int *kw, int layout, 
     for (int l = 0; l < n_layers; ++l) {
         p.win[l] = widths[l];
         p.wout[l] = widths[l + 1];
+        p.narrow[l] = layout == kPacked && l == n_layers - 1 && mlpl::narrow_last(kw, n_layers);
         p.mt[l] = mlpl::m_tiles(kw, l);
         p.kb[l] = mlpl::k_blocks(kw, l);
         if (layout == kPacked) {
@@ -97,6 +102,7 @@ void fill_pack_args_layered(const int *widths, int l0, int count, PackArgs &p)
         const size_t off = layered_layer_offset(widths, l0 + i);
         p.win[i] = win;
         p.wout[i] = wout;
+        p.narrow[i] = 0;
         p.mt[i] = layered_kout(wout) / 32;
         p.kb[i] = layered_kin(win) / 16;
         p.a_off[i] = (uint32_t)off;

@@ -132,9 +132,12 @@ def test_pack_without_a_device_reports_hip_error():
 
 
 def test_plan_widths():
-    assert B.mlp_plan_widths(workloads.get("small").widths) == [16, 32, 32, 32, 32, 32, 32, 32, 32]
-    assert B.mlp_plan_widths(workloads.get("page").widths) == [32] + [64] * 7 + [32]
-    assert B.mlp_plan_widths(workloads.get("hetero").widths) == [32, 64, 64, 64, 128, 64, 64, 32, 32]
+    # a 4-wide last layer on a dedicated FP16 kernel is computed 4 wide (16x16x32 MFMA)
+    assert B.mlp_plan_widths(workloads.get("small").widths) == [16, 32, 32, 32, 32, 32, 32, 32, 4]
+    assert B.mlp_plan_widths(workloads.get("page").widths) == [32] + [64] * 7 + [4]
+    assert B.mlp_plan_widths(workloads.get("hetero").widths) == [32, 64, 64, 64, 128, 64, 64, 32, 4]
+    assert B.mlp_plan_widths(workloads.get("stream").widths) == [64] * 8 + [32]
+    assert B.mlp_plan_widths(workloads.get("page").widths, B.MLP_LAYOUT_PACKED_FP8) == [32] + [64] * 7 + [32]
     assert B.mlp_plan_widths([2, 2, 1]) == [64, 64, 64]  # generic kernel, zero-padded to 64
     assert B.mlp_plan_widths([2, 65, 1]) == [128, 128, 128]  # a width above 64: the 128-wide family
     assert B.mlp_plan_widths([100, 300, 129, 7]) == [128, 384, 256, 128]  # layer by layer
@@ -195,6 +198,33 @@ def test_layered_image_layout(widths):
 #   layer >0: 16 kb + 8 (j // 4) + 4 g + j % 4
 # and the bias tile entry (mt, g, j) is b[32 mt + 8 (j // 4) + 4 g + j % 4].  Anything outside the real
 # matrix is 0.  MT = ceil(w_out / 32) output tiles, KB = ceil(w_in / 16) input blocks.
+#
+# A last layer of at most 4 outputs (a 16x16x32 MFMA over both 16-sample halves of a 32-sample
+# fragment) is laid out as [kb][lane][8]: lane = 16 a + i holds output i % 4 when i < 8 and
+# i // 4 == a % 2 (else zeros), over the slots of group a // 2; its bias tile starts with
+# b[0..3], b[0..3] (the C operand of lane groups a = 0 and 1) and is zero after.
+
+def _unpack_narrow(A, bias, KB):
+    full = np.zeros((4, KB * 16), np.uint16)
+    seen = np.zeros((4, KB * 16), bool)
+    for kb in range(KB):
+        for lane in range(64):
+            a, i = lane // 16, lane % 16
+            g = a // 2
+            for j in range(8):
+                f = 16 * kb + 8 * (j // 4) + 4 * g + j % 4
+                v = A[kb, lane, j]
+                if i < 8 and i // 4 == a % 2:
+                    r = i % 4
+                    # the two sample halves must carry the same weight
+                    assert not seen[r, f] or full[r, f] == v
+                    full[r, f], seen[r, f] = v, True
+                else:
+                    assert v == 0, "lane %d of a narrow fragment must be zero" % lane
+    assert seen.all()
+    assert np.array_equal(bias[0:4], bias[4:8]) and not bias[8:].any()
+    return full, bias[0:4].copy()
+
 
 def _unpack(image, kw, widths):
     L = len(widths) - 1
@@ -203,6 +233,15 @@ def _unpack(image, kw, widths):
     for l in range(L):
         MT = -(-kw[l + 1] // 32)
         KB = -(-kw[l] // 16)
+        if l == L - 1 and kw[L] <= 4:
+            A = image[off:off + KB * 1024].view(np.uint16).reshape(KB, 64, 8)
+            off += KB * 1024
+            bias = image[off:off + 128].view(np.float32)
+            off += 128
+            full, b4 = _unpack_narrow(A, bias, KB)
+            Ws.append(full)
+            bs.append(b4)
+            continue
         A = image[off:off + MT * KB * 1024].view(np.uint16).reshape(MT, KB, 2, 32, 8)
         off += MT * KB * 1024
         bias = image[off:off + MT * 128].view(np.float32).reshape(MT, 2, 16)

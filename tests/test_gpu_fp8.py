@@ -1,27 +1,37 @@
 """GPU parity of the FP8 kernels (MLP_LAYOUT_PACKED_FP8) against the oracle's FP8 network, through the
 C ABI, on the dedicated shapes.
 
-- integer-exact nets (every weight, every 16 h and every partial sum exact in E4M3 / binary32): bit for
-  bit against int64 products and the FP8 oracle;
+- order-free nets, bit for bit against the FP8 oracle:
+  - integer-exact nets (every weight, every 16 h and every partial sum exact in E4M3 / binary32);
+  - signed permutation chains: one nonzero weight per row, a power of two of either sign (so its E4M3
+    code is exact), zero or random biases (bias plus one product is a single binary32 rounding in
+    any order); every layer's input goes through E4M3(16 h) of both signs and every negative
+    pre-activation through the binary16 leaky slope;
+  - the eight-layer sign-alternating diagonal golden (tests/golden/fp8_sign_alternating_diag.json),
+    embedded in the small shape;
 - random weights at the workloads' initialisations, ragged row counts: the contract tolerance on every
   element and the FP8 bar below.
 
 The FP8 bar (its own tolerance: the contract's 1e-2 is stated for the FP16 network).  The kernel and
 the oracle quantise identically (the same E4M3 codes for the weights, the same scale per row, the same
-conversion of 16 h), so the only legitimate difference is the order of the binary32 sums inside the
-MFMA.  That moves a binary16 result by at most an ulp or so, which is harmless by itself; but when it
-takes the next layer's 16 h across an E4M3 rounding boundary, that activation moves by one E4M3 step,
-2^-4 .. 2^-3 of its size.  At these initialisations hidden activations are below ~1 and the next
-layer's weights ~fan_in^-1/2, so one such flip moves an output by up to ~0.02; a row rarely takes
-more than two.  Besides, the MFMA accumulates the 64 products of a block in its own order, so the
-final binary16 outputs differ from the oracle's sequential sums by an ulp (~1e-4) more often on
-wider layers (measured bit-identical: ~80 % of outputs at K = 64, ~63 % at K = 128).  Measured
-against the oracle: mean |d| <= 1e-3, max |d| ~0.026, 0.1-1.3 % of the elements beyond 1e-2 -- five
-to ten times less than FP8 quantisation itself moves the outputs from the FP16 network (mean ~0.005,
-max ~0.05).  The bar: every element within 0.05, mean |d| <= 2e-3, at most 2 % of the elements beyond
-the contract's 1e-2 (a wrong scale, slot order or missing activation breaks all three; the integer
-tests pin the indexing bit for bit).
+conversion of 16 h).  Every product of two E4M3 values has at most 8 significant bits, so at these
+initialisations the binary32 sums are exact in any order: the test checks that the network evaluated
+with exact sums (rounded once to binary32) gives the oracle's bits, so summation order alone explains
+no difference.  What remains is the FP8 MFMA's own accumulator, which need not be an IEEE binary32
+adder.  The bar models an accumulator accurate to half a binary16 ulp of each dot product (the
+precision of the layer's own FP16 result): the test evaluates the network with every layer's sums
+perturbed by a random relative error of up to 2^-11 before the binary16 rounding (two seeded draws)
+and takes the larger statistics of the two.  Such an error flips some binary16 roundings by one ulp,
+and a flip that takes the next layer's 16 h across an E4M3 rounding boundary moves that activation by
+a whole E4M3 step (2^-4 .. 2^-3 of its size): at these initialisations the outputs then move by up to
+~0.02-0.04, ~1e-3 on average.  The GPU passes if max |d| <= 1.5 x the model's max, mean |d| <= 1.25 x
+its mean and the count beyond the contract's 1e-2 <= 1.25 x its count + 2 (the factors cover the
+draw-to-draw spread of these statistics: the max varies by ~1.4x between draws, the mean and the count
+by ~10 %).  Sign, slope and indexing slips fail the bit-exact nets above.
 """
+import json
+from pathlib import Path
+
 import numpy as np
 import pytest
 
@@ -33,28 +43,118 @@ from mlp_neural_shading_amd import workloads
 pytestmark = pytest.mark.gpu
 
 FP8 = B.MLP_LAYOUT_PACKED_FP8
-FP8_MAX_ABS = 0.05
-FP8_MAX_MEAN = 2e-3
-FP8_MAX_BEYOND = 0.02
+GOLDEN = Path(__file__).parent / "golden" / "fp8_sign_alternating_diag.json"
 
 
 def f16(a):
     return np.asarray(a, dtype=np.float64).astype(np.float16)
 
 
-def _compare_fp8(g_bits, o_bits, what):
-    g = np.asarray(g_bits).view(np.float16).astype(np.float64)
+def _e4m3(x):
+    """E4M3 value nearest to x (nearest even), via PyTorch's float8_e4m3fn cast."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def _fp8_net(Ws, bs, x_bits, rng=None, rel=0.0):
+    """The FP8 network (the oracle's readings) with exact sums rounded once to binary32; with rel > 0
+    every sum is first scaled by (1 + u rel), u ~ U(-1, 1) per element (an accumulator error model)."""
+    s = np.uint16(0x211F).view(np.float16)  # half(0.01)
+    h = np.asarray(x_bits).view(np.float16).astype(np.float32)
+    L = len(Ws)
+    for l in range(L):
+        W = np.asarray(Ws[l]).view(np.float16).astype(np.float64)
+        amax = np.abs(W).max(axis=1)
+        E = np.zeros(W.shape[0])
+        nz = amax > 0
+        E[nz] = np.ceil(np.log2(amax[nz] / 448.0))
+        E[nz] += amax[nz] > 448.0 * 2.0 ** E[nz]  # guard the log2 rounding: smallest E with amax <= 448 2^E
+        E[nz] -= amax[nz] <= 448.0 * 2.0 ** (E[nz] - 1)
+        Wq = _e4m3((W / 2.0 ** E[:, None]).astype(np.float32)).astype(np.float64) * 2.0 ** E[:, None]
+        xq = _e4m3(np.float32(16) * h).astype(np.float64) / 16.0
+        acc = xq @ Wq.T + np.asarray(bs[l]).view(np.float16).astype(np.float64)[None, :]
+        if rel:
+            acc = acc * (1.0 + rel * rng.uniform(-1.0, 1.0, size=acc.shape))
+        v = acc.astype(np.float32).astype(np.float16)
+        if l + 1 < L:
+            v = np.maximum(v, (v * s).astype(np.float16))
+        h = v.astype(np.float32)
+    return h.astype(np.float16).view(np.uint16)
+
+
+def _stats(a_bits, o_bits):
+    a = np.asarray(a_bits).view(np.float16).astype(np.float64)
     o = np.asarray(o_bits).view(np.float16).astype(np.float64)
-    assert np.isfinite(g).all() and np.isfinite(o).all(), what
-    d = np.abs(g - o)
-    ok = (d <= CONTRACT_TOL) | (d <= CONTRACT_TOL * np.abs(o))
+    d = np.abs(a - o)
+    beyond = ~((d <= CONTRACT_TOL) | (d <= CONTRACT_TOL * np.abs(o)))
+    return d, beyond
+
+
+def _compare_fp8(g_bits, o_bits, Ws, bs, x_bits, what):
+    """GPU vs oracle against the bar of the accumulator error model (module docstring)."""
+    g = np.asarray(g_bits).view(np.float16).astype(np.float64)
+    assert np.isfinite(g).all(), what
+    assert np.array_equal(_fp8_net(Ws, bs, x_bits), o_bits), "%s: the sums are not order-free here" % what
+    model = [_stats(_fp8_net(Ws, bs, x_bits, np.random.default_rng(100 + k), 2.0 ** -11), o_bits) for k in range(2)]
+    m_max = max(d.max() for d, _ in model)
+    m_mean = max(d.mean() for d, _ in model)
+    m_beyond = max(int(b.sum()) for _, b in model)
+    d, beyond = _stats(g_bits, o_bits)
     same = float((np.asarray(g_bits) == np.asarray(o_bits)).mean())
-    log("  %s: max |d| %.3g, mean %.3g, bit-identical %.4f, beyond 1e-2: %d of %d"
-        % (what, d.max(), d.mean(), same, (~ok).sum(), d.size))
-    assert d.max() <= FP8_MAX_ABS, what
-    assert d.mean() <= FP8_MAX_MEAN, what
-    assert (~ok).mean() <= FP8_MAX_BEYOND, what
+    log("  %s: GPU max |d| %.3g, mean %.3g, beyond 1e-2 %d of %d, bit-identical %.4f; half-ulp model: max %.3g, "
+        "mean %.3g, beyond %d" % (what, d.max(), d.mean(), int(beyond.sum()), d.size, same, m_max, m_mean, m_beyond))
+    assert d.max() <= 1.5 * m_max, what
+    assert d.mean() <= 1.25 * m_mean, what
+    assert beyond.sum() <= 1.25 * m_beyond + 2, what
     return same
+
+
+def _signed_chain(widths, rng, diag=(1, -64, -1, -64, -1, -64, -1, 1), random_bias=False):
+    """One nonzero weight per row, diag[l] (a power of two, exact in E4M3 under its row scale), from a
+    random partial permutation; zero biases or random binary16 ones in [-0.1, 0.1]."""
+    L = len(widths) - 1
+    Ws, bs = [], []
+    for l in range(L):
+        win, wout = widths[l], widths[l + 1]
+        W = np.zeros((wout, win))
+        src = rng.permutation(max(win, wout))
+        for r in range(wout):
+            W[r, src[r] % win] = diag[l % len(diag)]
+        Ws.append(f16(W))
+        bs.append(f16(rng.uniform(-0.1, 0.1, size=wout) if random_bias else np.zeros(wout)))
+    return Ws, bs
+
+
+@pytest.mark.parametrize("random_bias", [False, True], ids=["zero-bias", "random-bias"])
+@pytest.mark.parametrize("name", list(workloads.ALIASES))
+def test_signed_permutation_chain_bit_exact(oracle_mod, name, random_bias):
+    rng = np.random.default_rng(57)
+    widths = workloads.get(name).widths
+    Ws, bs = _signed_chain(widths, rng, random_bias=random_bias)
+    x = f16(rng.uniform(-1, 1, size=(1000 + 13, widths[0]))).view(np.uint16)
+    ref = oracle_mod.mlp_forward_fp8(Ws, bs, x)
+    assert (ref.view(np.float16) < 0).any() and (ref.view(np.float16) > 0).any()
+    log("FP8 signed permutation chain", name, "random bias" if random_bias else "zero bias")
+    y = run(Ws, bs, x, layout=FP8)
+    assert np.array_equal(y, ref)
+
+
+def test_sign_alternating_golden_on_the_small_shape(oracle_mod):
+    """The golden's four-wide diagonal chain as the first four features of the small shape
+    (16 -> 32 x 7 -> 4, diagonal weights d_l on rows that have a same-index input, zero elsewhere)."""
+    g = json.loads(GOLDEN.read_text())
+    widths = workloads.get("small").widths
+    Ws = [f16(np.eye(widths[l + 1], widths[l]) * g["diag"][l]) for l in range(8)]
+    bs = [f16(np.zeros(widths[l + 1])) for l in range(8)]
+    rng = np.random.default_rng(3)
+    x = rng.uniform(-1, 1, size=(300, widths[0]))
+    x[:, :4] = np.array(g["x"])[None, :]
+    x = f16(x).view(np.uint16)
+    y = run(Ws, bs, x, layout=FP8)
+    want = np.array([int(v, 16) for v in g["y_bits"]], np.uint16)
+    assert (y == want[None, :]).all()
+    assert np.array_equal(y, oracle_mod.mlp_forward_fp8(Ws, bs, x))
 
 
 @pytest.mark.parametrize("name", list(workloads.ALIASES))
@@ -91,7 +191,7 @@ def test_random_weights(oracle_mod, name):
     log("FP8 random weights", name, "rows", rows)
     y = run(Ws, bs, xt, layout=FP8)
     ref = oracle_mod.mlp_forward_fp8(Ws, bs, xb, threads=host_threads())
-    _compare_fp8(y, ref, name)
+    _compare_fp8(y, ref, Ws, bs, xb, name)
     # and the FP8 network stays close to the FP16 one
     y16 = oracle_mod.mlp_forward(Ws, bs, xb, threads=host_threads())
     d = np.abs(y.view(np.float16).astype(np.float64) - y16.view(np.float16).astype(np.float64))

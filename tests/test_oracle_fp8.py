@@ -7,6 +7,8 @@ activations scaled by 16, FP32 accumulation, binary16 rounding and leaky ReLU).
 - the decoder against PyTorch on all 256 codes;
 - the row-scale rule (max |w| / 2^E within (224, 448]);
 - three hand-worked examples (tests/golden/fp8_hand.json, derivations inside);
+- an eight-layer sign-alternating diagonal net (tests/golden/fp8_sign_alternating_diag.json): the leaky
+  slope and the sign of E4M3(16 h) through every layer, re-derived in exact rational arithmetic;
 - integer-exact nets against int64 brute force, bit for bit;
 - the FP8 network stays close to the FP16 one at the workloads' initialisations.
 """
@@ -84,6 +86,50 @@ def test_hand_worked_examples(oracle_mod, case):
     if "hidden_bits" in case:
         y1 = oracle_mod.mlp_forward_fp8(W[:1], b[:1], x)
         assert [hex(int(v)) for v in oracle_mod.leaky_f16_bits(y1.ravel())] == case["hidden_bits"]
+
+
+def _rne(q, e_min, frac_bits):
+    """Nearest-even rounding of the rational q to a binary format with frac_bits fraction bits and
+    smallest normal exponent e_min (gradual underflow below), in exact rational arithmetic."""
+    from fractions import Fraction
+
+    if q == 0:
+        return Fraction(0)
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    step = Fraction(2) ** (max(e, e_min) - frac_bits)
+    n, rem = divmod(a, step)
+    n = int(n) + (1 if rem > step / 2 or (rem == step / 2 and int(n) % 2 == 1) else 0)
+    return (n * step) if q > 0 else -(n * step)
+
+
+def test_sign_alternating_diagonal_net_fp8(oracle_mod):
+    """tests/golden/fp8_sign_alternating_diag.json: the stored bits (derived by hand for x = -1) and a
+    re-derivation of all four rows in exact rational arithmetic (E4M3 and binary16 nearest-even
+    written here from their definitions), both against the oracle."""
+    from fractions import Fraction
+
+    g = json.loads((Path(__file__).parent / "golden" / "fp8_sign_alternating_diag.json").read_text())
+    d = g["diag"]
+    W = [_f16(np.eye(4) * dl) for dl in d]
+    b = [_f16(np.zeros(4)) for _ in d]
+    x = _f16(np.array(g["x"])[:, None] * np.ones((1, 4))).view(np.uint16)
+    y = oracle_mod.mlp_forward_fp8(W, b, x)
+    assert [hex(int(v)) for v in y[:, 0]] == g["y_bits"]
+    assert (y == y[:, :1]).all()
+    s = Fraction(1311, 2 ** 17)  # half(0.01)
+    for x0, want in zip(g["x"], g["y_values"]):
+        h = Fraction(x0)
+        for l, dl in enumerate(d):
+            acc = dl * _rne(16 * h, -6, 3) / 16  # one product, exact in binary32
+            h = _rne(acc, -14, 10)
+            if l + 1 < len(d) and h < 0:
+                h = _rne(h * s, -14, 10)
+        assert float(h) == want, (x0, float(h), want)
 
 
 @pytest.mark.parametrize("seed", range(6))

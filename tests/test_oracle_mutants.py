@@ -49,6 +49,10 @@ FP8_MUTANTS = {
                                "const double r = trunc(a / ldexp(1.0, e - 3));"),
     "fp8_saturating_encoder": ("if (a > 464.0)\n        return sign | 0x7f;", "if (a > 464.0)\n        return sign | 0x7e;"),
     "fp8_subnormal_scale": ("mag = ldexpf((float)f, -9);", "mag = ldexpf((float)f, -10);"),
+    # the FP8 network's own activation call and the sign of its encoder
+    "fp8_relu_not_leaky": ("                    v = oracle_leaky_f16(v);",
+                           "                    v = (v & 0x8000u) ? (uint16_t)0 : v;"),
+    "fp8_encoder_drops_sign": ("const uint8_t sign = signbit(x) ? 0x80 : 0;", "const uint8_t sign = 0;"),
 }
 
 
@@ -62,6 +66,7 @@ def _quick_pins_fp8(o):
         yield lambda case=case: fp8.test_hand_worked_examples(o, case)
     for seed in range(3):
         yield lambda seed=seed: fp8.test_integer_exact_nets_match_int64_brute_force(o, seed)
+    yield lambda: fp8.test_sign_alternating_diagonal_net_fp8(o)
     yield lambda: fp8.test_fp8_network_is_close_to_the_fp16_network(o, "page")
 
 
