@@ -146,6 +146,22 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
  * Errors: INVALID_ARGUMENT, NOT_PACKED, UNSUPPORTED, HIP (launch failure). */
 int mlp_infer(int64_t batch, const void *in_ptr, void *out_ptr, void *stream);
 
+/* mlp_infer for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, semantics and errors as mlp_infer,
+ * but it calls no hipMalloc, hipFree or pool allocation.  A fused network (the dedicated and generic
+ * kernels) uses no scratch memory, so there it runs exactly what mlp_infer runs.  A network beyond the
+ * fused limits keeps its intermediate activations in a fixed scratch array of 64 MiB per GPU (file-
+ * scope device memory, looked up on the first call on each device and held until the process ends)
+ * instead of the pool: rows run in blocks of as many row tiles (256 rows) as two blocks of activations
+ * at the widest hidden layer (padded to 64, FP16) fit in 64 MiB, e.g. 16,384 rows at width 1024 and
+ * 4,096 rows at width 4096; MLP_ERR_UNSUPPORTED if not even one row tile fits (never, within
+ * MLP_MAX_WIDTH).  The array keeps the last call's contents; every value a call reads from it was
+ * written earlier in the same call, so nothing needs clearing.  All calls on one GPU share that
+ * array: two calls whose work may overlap on the GPU (different streams, or different threads on the
+ * same stream without ordering) race on it and may corrupt each other's results; order them, e.g.
+ * one stream or events. */
+int mlp_infer_noalloc(int64_t batch, const void *in_ptr, void *out_ptr, void *stream);
+
 /* mlp_infer with an explicit activation form (MLP_ACT_VECTOR or MLP_ACT_SCALARISED). */
 int mlp_infer_ex(int64_t batch, const void *in_ptr, void *out_ptr, void *stream, int act_mode);
 

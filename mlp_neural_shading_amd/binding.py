@@ -34,7 +34,7 @@ MLP_FUSED_MAX_WIDTH = 128
 
 EXPORTED = (
     "mlp_packed_size", "mlp_plan_widths", "mlp_pack_host", "mlp_pack_weights", "mlp_pack_weights_device",
-    "mlp_infer",
+    "mlp_infer", "mlp_infer_noalloc",
     "mlp_infer_ex", "mlp_set_activation_mode", "mlp_kernel_name", "mlp_debug_read_packed",
     "mlp_last_error", "mlp_release",
 )
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
             "mlp_pack_weights": ([i32, p, p, p, i32, p], i32),
             "mlp_pack_weights_device": ([i32, p, p, p, i32, p], i32),
             "mlp_infer": ([i64, p, p, p], i32),
+            "mlp_infer_noalloc": ([i64, p, p, p], i32),
             "mlp_infer_ex": ([i64, p, p, p, i32], i32),
             "mlp_set_activation_mode": ([i32], i32),
             "mlp_kernel_name": ([i32, p, sz], i32),
@@ -164,6 +165,11 @@ def mlp_pack_weights_device(weight_ptrs, bias_ptrs, widths, layout: int = MLP_LA
 def mlp_infer(batch: int, in_ptr: int, out_ptr: int, stream=None) -> None:
     _check(lib().mlp_infer(int(batch), ctypes.c_void_p(in_ptr), ctypes.c_void_p(out_ptr), _stream(stream)),
            "mlp_infer")
+
+
+def mlp_infer_noalloc(batch: int, in_ptr: int, out_ptr: int, stream=None) -> None:
+    _check(lib().mlp_infer_noalloc(int(batch), ctypes.c_void_p(in_ptr), ctypes.c_void_p(out_ptr), _stream(stream)),
+           "mlp_infer_noalloc")
 
 
 def mlp_infer_ex(batch: int, in_ptr: int, out_ptr: int, stream=None, act_mode: int = MLP_ACT_VECTOR) -> None:

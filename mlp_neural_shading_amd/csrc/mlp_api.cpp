@@ -2,7 +2,7 @@
 //
 // Every argument is validated on the host before the first HIP call.  The library holds one packed
 // network (the current net) on the device that was current when it was packed.
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>  // HIP_SYMBOL and __device__ for the no-alloc scratch array
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -396,10 +396,39 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
 
 namespace {
 
-// The layered path: rows in blocks (see kLayeredScratchBytes), each block through every layer, with the
-// activations between layers in two scratch buffers allocated on the stream (stream-ordered, so
-// calls on different streams never share them) and freed on it afterwards.
-int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t stream)
+// The scratch array of mlp_infer_noalloc: file-scope device memory, one copy per GPU, held until the
+// process ends.  Host code never uses its name as an address: each device's address is looked up once
+// (hipGetSymbolAddress, with that device current) and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// This device's scratch address; looked up on the device's first call.  `device` must be current.
+int scratch_address(int device, void **out)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return fail(MLP_ERR_UNSUPPORTED, "device %d is beyond the %d devices mlp_infer_noalloc tracks", device, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void *ptr = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess)
+            return hip_fail(err, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[device] = ptr;
+    }
+    *out = g_scratch_ptr[device];
+    return MLP_OK;
+}
+
+// The layered path: rows in blocks, each block through every layer, with the activations between
+// layers in two scratch buffers.  Without `ext` the buffers are allocated on the stream (stream-ordered,
+// so calls on different streams never share them) and freed on it afterwards, with blocks as large as
+// kLayeredScratchBytes allows (at least kLayeredMinRows); with `ext` (ext_bytes of caller-provided
+// device memory) nothing is allocated and the blocks are as large as `ext` holds.
+int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t stream, void *ext = nullptr,
+                  size_t ext_bytes = 0)
 {
     const int L = g_net.n_layers;
     const int *w = g_net.widths;
@@ -407,11 +436,21 @@ int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t 
     for (int l = 1; l < L; ++l)
         ld_max = mlpk::layered_kin(w[l]) > ld_max ? mlpk::layered_kin(w[l]) : ld_max;
     const int64_t tile = mlpk::layered_rows_per_tile();
-    int64_t block = kLayeredScratchBytes / (2 * 2 * (int64_t)(ld_max > 0 ? ld_max : 1)) / tile * tile;
+    const int64_t row_bytes = 2 * 2 * (int64_t)(ld_max > 0 ? ld_max : 1);  // both buffers, FP16
+    int64_t block = kLayeredScratchBytes / row_bytes / tile * tile;
     block = block > kLayeredMinRows ? block : kLayeredMinRows;
+    if (ext) {
+        block = (int64_t)ext_bytes / row_bytes / tile * tile;
+        if (block < tile)
+            return fail(MLP_ERR_UNSUPPORTED, "one row tile of this network's activations needs %lld bytes, more than "
+                        "the %zu bytes of mlp_infer_noalloc's scratch", (long long)(tile * row_bytes), ext_bytes);
+    }
     const int64_t chunk = batch < block ? batch : block;
     void *buf[2] = {nullptr, nullptr};
-    if (L > 1) {
+    if (ext) {
+        buf[0] = ext;
+        buf[1] = (uint8_t *)ext + (size_t)chunk * ld_max * 2;  // chunk: a multiple of the tile, or the batch
+    } else if (L > 1) {
         hipMemPool_t pool = nullptr;
         const int rc = layered_pool(g_net.device, &pool);
         if (rc != MLP_OK)
@@ -451,19 +490,17 @@ int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t 
             err = mlpk::launch_layer(a, stream);
         }
     }
-    for (int i = 0; i < 2; ++i)
-        if (buf[i])
-            (void)hipFreeAsync(buf[i], stream);
+    if (!ext)
+        for (int i = 0; i < 2; ++i)
+            if (buf[i])
+                (void)hipFreeAsync(buf[i], stream);
     if (err != hipSuccess)
         return hip_fail(err, "layer kernel launch");
     return ok();
 }
 
-}  // namespace
-
-extern "C" {
-
-int mlp_infer_ex(int64_t batch, const void *in_ptr, void *out_ptr, void *stream, int act_mode)
+// mlp_infer_ex and mlp_infer_noalloc: validation, then the fused kernel or the layered path.
+int infer(int64_t batch, const void *in_ptr, void *out_ptr, void *stream, int act_mode, bool noalloc)
 {
     if (batch < 0)
         return fail(MLP_ERR_INVALID_ARGUMENT, "batch must be >= 0, got %lld", (long long)batch);
@@ -498,8 +535,15 @@ int mlp_infer_ex(int64_t batch, const void *in_ptr, void *out_ptr, void *stream,
         return fail(MLP_ERR_INVALID_ARGUMENT, "current device %d is not the device %d the network was packed on",
                     dev, g_net.device);
 
-    if (is_layered(e))
-        return infer_layered(batch, in_ptr, out_ptr, (hipStream_t)stream);
+    if (is_layered(e)) {
+        if (!noalloc)
+            return infer_layered(batch, in_ptr, out_ptr, (hipStream_t)stream);
+        void *ptr = nullptr;
+        rc = scratch_address(dev, &ptr);
+        if (rc != MLP_OK)
+            return rc;
+        return infer_layered(batch, in_ptr, out_ptr, (hipStream_t)stream, ptr, kNoAllocScratchBytes);
+    }
     const int64_t rows_per_block = (int64_t)e->rows_per_wave * (e->threads / 64);
     const int64_t blocks = (batch + rows_per_block - 1) / rows_per_block;
     const int grid = (int)(blocks < g_net.grid_cap[act_mode] ? blocks : g_net.grid_cap[act_mode]);
@@ -514,6 +558,20 @@ int mlp_infer_ex(int64_t batch, const void *in_ptr, void *out_ptr, void *stream,
     if (err != hipSuccess)
         return hip_fail(err, "kernel launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlp_infer_ex(int64_t batch, const void *in_ptr, void *out_ptr, void *stream, int act_mode)
+{
+    return infer(batch, in_ptr, out_ptr, stream, act_mode, false);
+}
+
+int mlp_infer_noalloc(int64_t batch, const void *in_ptr, void *out_ptr, void *stream)
+{
+    return infer(batch, in_ptr, out_ptr, stream, g_act_mode, true);
 }
 
 int mlp_infer(int64_t batch, const void *in_ptr, void *out_ptr, void *stream)
