@@ -65,12 +65,26 @@ __device__ __forceinline__ h8 leaky_scalarised(h8 v)
     return v;
 }
 
+// An LDS address voff + soff with a constant soff: a ds_read's immediate offset has 16 bits, so an
+// soff of 64 KB or more is split into a 64 KB-aligned part added to voff (one register for every read
+// that shares voff and that part: the empty asm hides the sum from constant folding, so the compiler
+// computes it once rather than a register per distinct offset) and the rest as the immediate.
+__device__ __forceinline__ const uint8_t *lds_addr(const uint8_t *base, int voff, int soff)
+{
+    if (soff >= 65536) {
+        int vb = voff + (soff & ~0xffff);
+        asm("" : "+v"(vb));
+        return base + vb + (soff & 0xffff);
+    }
+    return base + voff + soff;
+}
+
 // Where the weight image is read from.  Offsets are split into a per-lane part (voff, a VGPR) and
 // a wave-uniform constant part (soff) so that neither path needs a register per fragment address.
 struct LdsSource {  // image staged in LDS: ds_read with the constant as an immediate offset
     const uint8_t *base;
-    __device__ __forceinline__ h8 load16(int voff, int soff) const { return *(const h8 *)(base + voff + soff); }
-    __device__ __forceinline__ h4 load8(int voff, int soff) const { return *(const h4 *)(base + voff + soff); }
+    __device__ __forceinline__ h8 load16(int voff, int soff) const { return *(const h8 *)lds_addr(base, voff, soff); }
+    __device__ __forceinline__ h4 load8(int voff, int soff) const { return *(const h4 *)lds_addr(base, voff, soff); }
 };
 
 struct BufferSource {  // image read through the caches with buffer loads (constant offset in an SGPR)
@@ -85,25 +99,30 @@ struct BufferSource {  // image read through the caches with buffer loads (const
     }
 };
 
-// Images larger than LDS (packed layout): the whole layers that fit are staged into LDS and read
-// from there, the rest through the caches.  SPLIT is the byte offset where the cached part begins;
-// which of the two a layer uses is decided at compile time (Body::ld16), per layer.
-template <int SPLIT>
+// Images larger than LDS: the leading LAYERS whole layers are staged into LDS (row-major rows padded
+// as in a fully staged image) and read from there, the rest through the caches; which of the two a
+// layer uses is decided at compile time (Body::in_lds), per layer, for either layout.
+template <int LAYERS>
 struct HybridSource {
-    static constexpr int kSplit = SPLIT;
+    static constexpr int kLayers = LAYERS;
     const uint8_t *base;
     __amdgpu_buffer_rsrc_t rsrc;
-    __device__ __forceinline__ h8 lds16(int voff, int soff) const { return *(const h8 *)(base + voff + soff); }
+    __device__ __forceinline__ h8 lds16(int voff, int soff) const { return *(const h8 *)lds_addr(base, voff, soff); }
+    __device__ __forceinline__ h4 lds8(int voff, int soff) const { return *(const h4 *)lds_addr(base, voff, soff); }
     __device__ __forceinline__ h8 buf16(int voff, int soff) const
     {
         return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
+    }
+    __device__ __forceinline__ h4 buf8(int voff, int soff) const
+    {
+        return __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, 0));
     }
 };
 
 template <class S>
 struct is_hybrid : std::false_type {};
-template <int SPLIT>
-struct is_hybrid<HybridSource<SPLIT>> : std::true_type {};
+template <int LAYERS>
+struct is_hybrid<HybridSource<LAYERS>> : std::true_type {};
 
 // LDS the staged weight image may use (the CU has 160 KB; a little is left for the kernel's own).
 constexpr int kLdsImageBudget = 159 * 1024;
@@ -121,13 +140,19 @@ struct Net {
     static constexpr size_t image_bytes(int layout) { return layout == kPacked ? mlpl::pk_bytes(w, L) : mlpl::rm_bytes(w, L); }
     // Bytes of the image as staged in LDS (row-major rows are padded there).
     static constexpr size_t lds_bytes(int layout) { return layout == kPacked ? mlpl::pk_bytes(w, L) : mlpl::rml_bytes(w, L); }
-    // Packed layout: bytes of the longest run of whole layers, from layer 0, within the LDS budget.
-    static constexpr int lds_prefix()
+    // The longest run of whole layers, from layer 0, whose LDS copy fits the budget, and the bytes of
+    // that prefix in the image (as stored) and in LDS (as staged).
+    static constexpr size_t lds_off(int layout, int l) { return layout == kPacked ? mlpl::pk_a_off(w, l) : mlpl::rml_w_off(w, l); }
+    static constexpr int lds_layers(int layout)
     {
         int l = 0;
-        while (l < L && mlpl::pk_a_off(w, l + 1) <= (size_t)kLdsImageBudget)
+        while (l < L && lds_off(layout, l + 1) <= (size_t)kLdsImageBudget)
             ++l;
-        return (int)mlpl::pk_a_off(w, l);
+        return l;
+    }
+    static constexpr int prefix_image_bytes(int layout, int p)
+    {
+        return (int)(layout == kPacked ? mlpl::pk_a_off(w, p) : mlpl::rm_w_off(w, p));
     }
 };
 
@@ -166,18 +191,38 @@ struct Body {
 
     // ---- weight delivery ------------------------------------------------------------------
 
-    // A 16-byte read of layer l's part of the packed image; with a hybrid source, from LDS if the
-    // whole layer lies before the split, else through the caches.
+    // Whether layer l is read from LDS (then a row-major layer has padded rows) or through the caches.
+    static constexpr bool in_lds(int l)
+    {
+        if constexpr (is_hybrid<Src>::value)
+            return l < Src::kLayers;
+        else
+            return LDS_W;
+    }
+
+    // 16- and 8-byte reads of layer l's part of the image, from LDS or through the caches.
     template <int l>
     static __device__ __forceinline__ h8 ld16(const Src &src, int voff, int soff)
     {
         if constexpr (is_hybrid<Src>::value) {
-            if constexpr (mlpl::pk_a_off(N::w, l + 1) <= (size_t)Src::kSplit)
+            if constexpr (in_lds(l))
                 return src.lds16(voff, soff);
             else
                 return src.buf16(voff, soff);
         } else {
             return src.load16(voff, soff);
+        }
+    }
+    template <int l>
+    static __device__ __forceinline__ h4 ld8(const Src &src, int voff, int soff)
+    {
+        if constexpr (is_hybrid<Src>::value) {
+            if constexpr (in_lds(l))
+                return src.lds8(voff, soff);
+            else
+                return src.buf8(voff, soff);
+        } else {
+            return src.load8(voff, soff);
         }
     }
 
@@ -186,28 +231,29 @@ struct Body {
     {
         constexpr int KB = N::KB(l);
         if constexpr (LAYOUT == kPacked) {
-            return ld16<l>(src, lane * 16, (int)mlpl::pk_a_off(N::w, l) + (mt * KB + kb) * mlpl::kFragBytes);
+            constexpr int a_off = (int)mlpl::pk_a_off(N::w, l);  // constant-evaluated, not computed per wave
+            return ld16<l>(src, lane * 16, a_off + (mt * KB + kb) * mlpl::kFragBytes);
         } else {
             // Row-major [out][in]: lane (g, m) gathers row 32 mt + m at its slot features.  In LDS
             // the rows are padded (mlp_layout.h), in global memory they are as given.
             constexpr int win = N::w[l], wout = N::w[l + 1];
             static_assert(win % 8 == 0, "row-major layers need w_in % 8 == 0");
-            constexpr int stride = LDS_W ? mlpl::rml_stride(l, win) : win * 2;
-            constexpr int w_off = LDS_W ? (int)mlpl::rml_w_off(N::w, l) : (int)mlpl::rm_w_off(N::w, l);
+            constexpr int stride = in_lds(l) ? mlpl::rml_stride(l, win) : win * 2;
+            constexpr int w_off = in_lds(l) ? (int)mlpl::rml_w_off(N::w, l) : (int)mlpl::rm_w_off(N::w, l);
             const int g = lane >> 5, m = lane & 31;
             const int r = 32 * mt + m;
             const int row = w_off + 32 * mt * stride;  // wave-uniform
             h8 a = (h8)(_Float16)0;
             if constexpr (l == 0) {
                 if (r < wout && 16 * kb + 8 * g < win)
-                    a = src.load16(m * stride + 8 * g * 2, row + 16 * kb * 2);
+                    a = ld16<l>(src, m * stride + 8 * g * 2, row + 16 * kb * 2);
             } else {
                 const int f0 = 16 * kb + 4 * g, f1 = f0 + 8;
                 h4 lo = (h4)(_Float16)0, hi = (h4)(_Float16)0;
                 if (r < wout && f0 < win)
-                    lo = src.load8(m * stride + 4 * g * 2, row + 16 * kb * 2);
+                    lo = ld8<l>(src, m * stride + 4 * g * 2, row + 16 * kb * 2);
                 if (r < wout && f1 < win)
-                    hi = src.load8(m * stride + 4 * g * 2, row + (16 * kb + 8) * 2);
+                    hi = ld8<l>(src, m * stride + 4 * g * 2, row + (16 * kb + 8) * 2);
                 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
             return a;
@@ -219,7 +265,8 @@ struct Body {
     {
         const int g = lane >> 5;
         if constexpr (LAYOUT == kPacked) {
-            const int soff = (int)mlpl::pk_b_off(N::w, l) + mt * mlpl::kBiasTileBytes;
+            constexpr int b_off = (int)mlpl::pk_b_off(N::w, l);
+            const int soff = b_off + mt * mlpl::kBiasTileBytes;
             const f4 b0 = __builtin_bit_cast(f4, ld16<l>(src, g * 64, soff));
             const f4 b1 = __builtin_bit_cast(f4, ld16<l>(src, g * 64 + 16, soff));
             const f4 b2 = __builtin_bit_cast(f4, ld16<l>(src, g * 64 + 32, soff));
@@ -230,13 +277,14 @@ struct Body {
         } else {
             constexpr int wout = N::w[l + 1];
             static_assert(wout % 4 == 0, "row-major layer needs w_out % 4 == 0");
-            const int soff = (LDS_W ? (int)mlpl::rml_b_off(N::w, l) : (int)mlpl::rm_b_off(N::w, l)) + 32 * mt * 2;
+            constexpr int b_off = in_lds(l) ? (int)mlpl::rml_b_off(N::w, l) : (int)mlpl::rm_b_off(N::w, l);
+            const int soff = b_off + 32 * mt * 2;
             h4 q[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 q[k] = (h4)(_Float16)0;
                 if (32 * mt + 8 * k + 4 * g < wout)
-                    q[k] = src.load8((8 * k + 4 * g) * 2, soff);
+                    q[k] = ld8<l>(src, (8 * k + 4 * g) * 2, soff);
             }
             const h8 lo = __builtin_shufflevector(q[0], q[1], 0, 1, 2, 3, 4, 5, 6, 7);
             const h8 hi = __builtin_shufflevector(q[2], q[3], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -255,27 +303,28 @@ struct Body {
     static __device__ __forceinline__ h8 narrow_frag(const Src &src, int kb, int lane)
     {
         if constexpr (LAYOUT == kPacked) {
-            return ld16<l>(src, lane * 16, (int)mlpl::pk_a_off(N::w, l) + kb * mlpl::kFragBytes);
+            constexpr int a_off = (int)mlpl::pk_a_off(N::w, l);
+            return ld16<l>(src, lane * 16, a_off + kb * mlpl::kFragBytes);
         } else {
             // gathered from the row-major matrix: row narrow_row(lane), the slot features of group g
             constexpr int win = N::w[l], wout = N::w[l + 1];
             static_assert(win % 8 == 0, "row-major layers need w_in % 8 == 0");
-            constexpr int stride = LDS_W ? mlpl::rml_stride(l, win) : win * 2;
-            constexpr int w_off = LDS_W ? (int)mlpl::rml_w_off(N::w, l) : (int)mlpl::rm_w_off(N::w, l);
+            constexpr int stride = in_lds(l) ? mlpl::rml_stride(l, win) : win * 2;
+            constexpr int w_off = in_lds(l) ? (int)mlpl::rml_w_off(N::w, l) : (int)mlpl::rm_w_off(N::w, l);
             const int g = lane >> 5, r = mlpl::narrow_row(lane);
             const bool live = r >= 0 && r < wout;
             const int m = live ? r : 0;
             h8 a = (h8)(_Float16)0;
             if constexpr (l == 0) {
                 if (live && 16 * kb + 8 * g < win)
-                    a = src.load16(m * stride + 8 * g * 2, w_off + 16 * kb * 2);
+                    a = ld16<l>(src, m * stride + 8 * g * 2, w_off + 16 * kb * 2);
             } else {
                 const int f0 = 16 * kb + 4 * g, f1 = f0 + 8;
                 h4 lo = (h4)(_Float16)0, hi = (h4)(_Float16)0;
                 if (live && f0 < win)
-                    lo = src.load8(m * stride + 4 * g * 2, w_off + 16 * kb * 2);
+                    lo = ld8<l>(src, m * stride + 4 * g * 2, w_off + 16 * kb * 2);
                 if (live && f1 < win)
-                    hi = src.load8(m * stride + 4 * g * 2, w_off + (16 * kb + 8) * 2);
+                    hi = ld8<l>(src, m * stride + 4 * g * 2, w_off + (16 * kb + 8) * 2);
                 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
             return a;
@@ -287,11 +336,12 @@ struct Body {
     static __device__ __forceinline__ f4 narrow_bias(const Src &src, int lane)
     {
         if constexpr (LAYOUT == kPacked) {
-            return __builtin_bit_cast(f4, ld16<l>(src, (lane >> 4) * 16, (int)mlpl::pk_b_off(N::w, l)));
+            constexpr int b_off = (int)mlpl::pk_b_off(N::w, l);
+            return __builtin_bit_cast(f4, ld16<l>(src, (lane >> 4) * 16, b_off));
         } else {
             // b [w_out] FP16, its section zero-padded to 16 bytes
-            const int soff = LDS_W ? (int)mlpl::rml_b_off(N::w, l) : (int)mlpl::rm_b_off(N::w, l);
-            h4 q = src.load8(0, soff);
+            constexpr int soff = in_lds(l) ? (int)mlpl::rml_b_off(N::w, l) : (int)mlpl::rm_b_off(N::w, l);
+            h4 q = ld8<l>(src, 0, soff);
             if (lane >= 32)
                 q = (h4)(_Float16)0;
             return __builtin_convertvector(q, f4);
@@ -695,9 +745,9 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
 {
     // Weights: the whole image in LDS (LDS_W), else the layers that fit in LDS and the rest through
     // the caches (packed layout), else everything through the caches.
-    constexpr int kSplit = (!LDS_W && LAYOUT == kPacked) ? N::lds_prefix() : 0;
+    constexpr int kLdsLayers = !LDS_W ? N::lds_layers(LAYOUT) : 0;
     using Src = typename std::conditional<
-        LDS_W, LdsSource, typename std::conditional<(kSplit > 0), HybridSource<kSplit>, BufferSource>::type>::type;
+        LDS_W, LdsSource, typename std::conditional<(kLdsLayers > 0), HybridSource<kLdsLayers>, BufferSource>::type>::type;
     using B = Body<N, NT, LAYOUT, ACT, GENERIC, LDS_W, Src, (EU < 3 && LDS_W)>;
     constexpr int bytes = (int)N::image_bytes(LAYOUT);
     constexpr int lbytes = (int)N::lds_bytes(LAYOUT);
@@ -731,12 +781,18 @@ __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu
         else
             stage_store_rowmajor<N, bytes, WAVES * 64>(lds, chunks, std::make_integer_sequence<int, kChunks>());
         src.base = lds;
-    } else if constexpr (kSplit > 0) {
-        __shared__ __attribute__((aligned(16))) uint8_t lds[kSplit];
-        constexpr int kChunks = (kSplit + WAVES * 64 * 16 - 1) / (WAVES * 64 * 16);
-        const auto chunks = stage_load<kSplit, WAVES * 64>(a.image, std::make_integer_sequence<int, kChunks>());
+    } else if constexpr (kLdsLayers > 0) {
+        // the leading kLdsLayers layers: kPrefix bytes of the image, kLdsPrefix bytes in LDS
+        constexpr int kPrefix = N::prefix_image_bytes(LAYOUT, kLdsLayers);
+        constexpr int kLdsPrefix = (int)N::lds_off(LAYOUT, kLdsLayers);
+        __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsPrefix];
+        constexpr int kChunks = (kPrefix + WAVES * 64 * 16 - 1) / (WAVES * 64 * 16);
+        const auto chunks = stage_load<kPrefix, WAVES * 64>(a.image, std::make_integer_sequence<int, kChunks>());
         B::load_inputs(B0, a, (tile < hi ? tile : lo) * kRows, lane, std::make_integer_sequence<int, NT>());
-        stage_store<kSplit, WAVES * 64>(lds, chunks, std::make_integer_sequence<int, kChunks>());
+        if constexpr (LAYOUT == kPacked)
+            stage_store<kPrefix, WAVES * 64>(lds, chunks, std::make_integer_sequence<int, kChunks>());
+        else
+            stage_store_rowmajor<N, kPrefix, WAVES * 64>(lds, chunks, std::make_integer_sequence<int, kChunks>());
         src.base = lds;
         src.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.image, 0, bytes, kBufferRsrcWord3);
     } else {
