@@ -48,7 +48,7 @@ enum {
                               /* power-of-two scale per output row (the smallest keeping the row  */
                               /* within 448), each layer's input stored as E4M3(16 h), FP32       */
                               /* accumulation, then FP16 rounding and leaky ReLU as in FP16; for  */
-                              /* the dedicated shapes, vector activation, host packing only       */
+                              /* the dedicated shapes and the vector activation                   */
 };
 
 /* Activation forms ("Bad versus good activation"); both compute the same function, bit for bit. */
@@ -108,9 +108,9 @@ int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const 
  * `stream` ("Row-major versus InferencingOptimal weights": the conversion can be recorded into the
  * GPU's command stream instead of run on the host).  The resulting device image is bit for bit the
  * one mlp_pack_weights builds, and it becomes the current network.
- *   layout    MLP_LAYOUT_PACKED (every shape, fused or layer by layer) or MLP_LAYOUT_ROW_MAJOR (the
- *             dedicated shapes); MLP_LAYOUT_PACKED_FP8 returns MLP_ERR_UNSUPPORTED before any HIP
- *             call (its per-row scales and E4M3 rounding are written by the host packer only)
+ *   layout    MLP_LAYOUT_PACKED (every shape, fused or layer by layer), MLP_LAYOUT_ROW_MAJOR or
+ *             MLP_LAYOUT_PACKED_FP8 (the dedicated shapes; the kernel computes each row's scale and
+ *             rounds to E4M3 exactly as the host packer does)
  *   d_weights n_layers host-memory entries, each a device pointer to [widths[l+1]][widths[l]] FP16
  *             row-major, 2-byte aligned
  *   d_biases  n_layers host-memory entries, each a device pointer to [widths[l+1]] FP16

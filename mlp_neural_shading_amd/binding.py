@@ -37,6 +37,8 @@ EXPORTED = (
     "mlp_infer", "mlp_infer_noalloc",
     "mlp_infer_ex", "mlp_set_activation_mode", "mlp_kernel_name", "mlp_debug_read_packed",
     "mlp_last_error", "mlp_release",
+    # include/mlp_testing.h
+    "mlp_testing_pack_device_on_host",
 )
 
 
@@ -70,6 +72,7 @@ def lib() -> ctypes.CDLL:
             "mlp_debug_read_packed": ([p, sz], i32),
             "mlp_last_error": ([], ctypes.c_char_p),
             "mlp_release": ([], None),
+            "mlp_testing_pack_device_on_host": ([i32, p, p, p, i32, p, sz, p], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -195,6 +198,18 @@ def mlp_debug_read_packed(nbytes: int) -> np.ndarray:
 
 def mlp_release() -> None:
     lib().mlp_release()
+
+
+def mlp_testing_pack_device_on_host(weights, biases, layout: int = MLP_LAYOUT_PACKED, widths=None):
+    """The device conversion kernel's work items run on the host: (image, exact_cover)."""
+    ws = _Weights(weights, biases)
+    w = _widths(ws.widths if widths is None else widths)
+    n = mlp_packed_size(w, layout)
+    dst = np.zeros(n, dtype=np.uint8)
+    cover = ctypes.c_int(-1)
+    _check(lib().mlp_testing_pack_device_on_host(len(w) - 1, w.ctypes.data, ws.wp, ws.bp, layout, dst.ctypes.data, n,
+                                                 ctypes.byref(cover)), "mlp_testing_pack_device_on_host")
+    return dst, bool(cover.value)
 
 
 # ---- torch convenience ------------------------------------------------------------------------

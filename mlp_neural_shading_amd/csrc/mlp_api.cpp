@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "mlp.h"
+#include "mlp_testing.h"
 #include "mlp_layered.h"
 #include "mlp_layout.h"
 #include "mlp_pack.h"
@@ -349,6 +350,42 @@ int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const 
     return ok();
 }
 
+int mlp_testing_pack_device_on_host(int n_layers, const int32_t *widths, const uint16_t *const *weights,
+                                    const uint16_t *const *biases, int layout, void *host_dst, size_t dst_bytes,
+                                    int *exact_cover)
+{
+    const KernelEntry *e = nullptr;
+    int rc = plan(n_layers, widths, layout, &e);
+    if (rc == MLP_OK)
+        rc = check_weights(n_layers, weights, biases);
+    if (rc != MLP_OK)
+        return rc;
+    const size_t need = state_image_bytes(n_layers, widths, layout, e);
+    if (!host_dst || !exact_cover)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "host_dst or exact_cover is NULL");
+    if (dst_bytes != need)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "host_dst holds %zu bytes, the image has %zu", dst_bytes, need);
+    std::vector<uint8_t> written(need, 0);
+    bool clean = true;
+    for (int l0 = 0; l0 < n_layers; l0 += 8) {  // as mlp_pack_weights_device launches it
+        const int count = n_layers - l0 < 8 ? n_layers - l0 : 8;
+        mlpk::PackArgs args{};
+        if (is_layered(e))
+            mlpk::fill_pack_args_layered(widths, l0, count, args);
+        else
+            mlpk::fill_pack_args(n_layers, widths, e->widths, layout, args);
+        for (int i = 0; i < count; ++i) {
+            args.w[i] = weights[l0 + i];
+            args.b[i] = biases[l0 + i];
+        }
+        clean &= mlpk::pack_items_on_host(args, count, (uint8_t *)host_dst, need, written);
+    }
+    for (size_t k = 0; k < need && clean; ++k)
+        clean = written[k] == 1;
+    *exact_cover = clean ? 1 : 0;
+    return ok();
+}
+
 int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *const *d_weights,
                             const void *const *d_biases, int layout, void *stream)
 {
@@ -358,10 +395,6 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
         rc = check_weights(n_layers, (const uint16_t *const *)d_weights, (const uint16_t *const *)d_biases);
     if (rc != MLP_OK)
         return rc;
-    // The conversion kernel writes the FP16 images (packed and row-major) only.
-    if (layout == MLP_LAYOUT_PACKED_FP8)
-        return fail(MLP_ERR_UNSUPPORTED, "the device conversion writes the FP16 layouts only; pack the FP8 "
-                    "layout with mlp_pack_weights");
     for (int l = 0; l < n_layers; ++l)
         if (((uintptr_t)d_weights[l] | (uintptr_t)d_biases[l]) & 1)
             return fail(MLP_ERR_INVALID_ARGUMENT, "d_weights[%d] or d_biases[%d] is not 2-byte aligned", l, l);

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "mlp_registry.h"
 
 namespace mlpk {
@@ -18,15 +20,17 @@ size_t image_bytes(int n_layers, const int *kernel_widths, int layout);
 void pack_image(int n_layers, const int *widths, const int *kernel_widths, const uint16_t *const *weights,
                 const uint16_t *const *biases, int layout, uint8_t *dst);
 
-// Everything the device packer needs, per layer l (kernel argument, passed by value).  first[l] is
-// the number of work items of the first section (packed: A-fragment slices; row-major: 16-byte
-// chunks of W), items[l] the total; a_off / b_off are the byte offsets of the two sections.
+// Everything the device packer needs, per layer l (kernel argument, passed by value).  Work items
+// [0, first[l]) write the first section (packed: A-fragment slices; row-major: 16-byte chunks of W;
+// FP8: 32-byte lane slices of the A fragments), [first[l], mid[l]) the FP8 scale codes (empty for
+// the FP16 layouts), [mid[l], items[l]) the biases; a_off / s_off / b_off are the byte offsets of
+// the sections.
 struct PackArgs {
     const uint16_t *w[8];
     const uint16_t *b[8];
     int win[8], wout[8], mt[8], kb[8];
     int narrow[8];  // 1: the narrow last-layer layout of mlp_layout.h (packed layout, one output tile)
-    uint32_t a_off[8], b_off[8], first[8], items[8];
+    uint32_t a_off[8], s_off[8], b_off[8], first[8], mid[8], items[8];
     int layout;
     int natural;  // 1: every layer in natural K order (the layered image), 0: the fused kernels' order
     uint8_t *dst;
@@ -47,5 +51,10 @@ void fill_pack_args_layered(const int *widths, int l0, int count, PackArgs &p);
 // Enqueue the device packer on `stream`: it writes the image pack_image would write, from device
 // copies of the weights (p.w, p.b) into p.dst.
 hipError_t launch_pack(const PackArgs &p, int n_layers, hipStream_t stream);
+
+// Run the device packer's work items on the host, from host weights (p.w, p.b) into dst (bytes long),
+// marking each byte written in `written` (bytes entries): false if any item writes outside
+// [0, bytes) or onto a byte written before (the kernel's own per-item code, checked on the CPU).
+bool pack_items_on_host(const PackArgs &p, int n_layers, uint8_t *dst, size_t bytes, std::vector<uint8_t> &written);
 
 }  // namespace mlpk

@@ -26,7 +26,8 @@ def _have_gpu() -> bool:
 
 
 def test_library_exports_every_declared_function():
-    decls = set(re.findall(r"^\s*(?:int|void|const char \*)\s*(mlp_\w+)\s*\(", HEADER.read_text(), re.M))
+    text = HEADER.read_text() + (ROOT / "include" / "mlp_testing.h").read_text()
+    decls = set(re.findall(r"^\s*(?:int|void|const char \*)\s*(mlp_\w+)\s*\(", text, re.M))
     assert decls == set(B.EXPORTED)
     L = B.lib()
     for name in decls:
@@ -88,21 +89,28 @@ def test_device_pack_validation():
     assert L.mlp_pack_weights_device(2, w3.ctypes.data, two, two, B.MLP_LAYOUT_ROW_MAJOR, None) == B.MLP_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("name", ["small", "page", "hetero", "wide", "stream"])
-def test_device_pack_refuses_the_fp8_layout(name):
-    """The conversion kernel writes the FP16 images only: an FP8 request on a shape that has an FP8
-    kernel must come back UNSUPPORTED before any HIP call (here, with or without a GPU), and the
-    current network must stay as it was."""
-    L = B.lib()
-    wl = workloads.get(name)
-    w = np.asarray(wl.widths, np.int32)
-    n = len(w) - 1
-    assert B.mlp_packed_size(w, B.MLP_LAYOUT_PACKED_FP8) > 0  # the host packer serves it
-    ptrs = (ctypes.c_void_p * n)(*[0x10000 * (i + 1) for i in range(n)])
-    B.mlp_release()
-    assert L.mlp_pack_weights_device(n, w.ctypes.data, ptrs, ptrs, B.MLP_LAYOUT_PACKED_FP8, None) == B.MLP_ERR_UNSUPPORTED
-    assert "FP16 layouts only" in B.mlp_last_error()
-    assert _err(B.mlp_kernel_name, 0) == B.MLP_ERR_NOT_PACKED  # nothing was installed
+DEVICE_PACK_CASES = [(name, layout) for name in ["small", "page", "hetero", "wide", "stream"]
+                     for layout in (B.MLP_LAYOUT_PACKED, B.MLP_LAYOUT_ROW_MAJOR, B.MLP_LAYOUT_PACKED_FP8)]
+DEVICE_PACK_CASES += [("generic-5-7-3", B.MLP_LAYOUT_PACKED), ("generic-100-30-7", B.MLP_LAYOUT_PACKED),
+                      ("layered-100-300-129-7", B.MLP_LAYOUT_PACKED), ("layered-40x11", B.MLP_LAYOUT_PACKED)]
+
+
+@pytest.mark.parametrize("name,layout", DEVICE_PACK_CASES)
+def test_device_conversion_items_run_on_the_host(name, layout):
+    """The device conversion kernel's own per-item code, run on the host over every work item: each
+    byte of the image is written exactly once and nothing outside it, and the image equals the host
+    packer's (weights with both signs and a wide range of magnitudes, so the FP8 row scales differ)."""
+    if name.startswith("generic") or name.startswith("layered"):
+        parts = name.split("-")[1:]
+        widths = tuple(int(p.split("x")[0]) for p in parts for _ in range(int(p.split("x")[1]) if "x" in p else 1))
+    else:
+        widths = workloads.get(name).widths
+    Ws, bs = workloads.init_weights(widths, seed=13)
+    rng = np.random.default_rng(13)
+    Ws = [(np.asarray(W, np.float64) * np.exp2(rng.integers(-6, 7, size=(W.shape[0], 1)))).astype(np.float16) for W in Ws]
+    image, exact = B.mlp_testing_pack_device_on_host(Ws, bs, layout, widths=widths)
+    assert exact, "a work item writes outside the image or over another item's bytes, or a byte stays unwritten"
+    assert np.array_equal(image, B.mlp_pack_host(Ws, bs, layout, widths=widths))
 
 
 @pytest.mark.skipif(_have_gpu(), reason="checks the error path taken when no GPU is visible")

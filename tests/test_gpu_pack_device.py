@@ -1,8 +1,9 @@
 """GPU tests of the device-side weight conversion (mlp_pack_weights_device, the conversion run as a
 kernel in the stream, "Row-major versus InferencingOptimal weights"): its image must equal the host
 packer's bit for bit -- the host packer's own layout is pinned on the CPU by test_abi_host.py's
-independent unpacker -- for every dedicated shape and layout and for shapes served by the generic
-kernels, and it must be stream-ordered."""
+independent unpacker, and the kernel's per-item code is run on the CPU over every work item there
+(extents and contents) before it runs here -- for every dedicated shape and layout (packed, row-major
+and FP8) and for shapes served by the generic kernels, and it must be stream-ordered."""
 import numpy as np
 import pytest
 
@@ -14,7 +15,7 @@ from gpu_util import device, log, run, to_device
 pytestmark = pytest.mark.gpu
 
 CASES = [(name, layout) for name in workloads.WORKLOADS
-         for layout in (B.MLP_LAYOUT_PACKED, B.MLP_LAYOUT_ROW_MAJOR)]
+         for layout in (B.MLP_LAYOUT_PACKED, B.MLP_LAYOUT_ROW_MAJOR, B.MLP_LAYOUT_PACKED_FP8)]
 GENERIC = [(5, 7, 3), (2, 2, 1), (128,) * 9, (1, 128, 1), (17, 33, 65, 100, 3)]
 
 
@@ -80,4 +81,24 @@ def test_inference_after_device_pack_is_stream_ordered():
         B.mlp_infer(x.shape[0], x.data_ptr(), out.data_ptr(), side.cuda_stream)
     side.synchronize()
     got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, expect)
+
+
+@pytest.mark.parametrize("name", list(workloads.ALIASES))
+def test_fp8_inference_after_device_pack(name):
+    """FP8 weights converted on the device (row scales of several magnitudes) give the bits of the
+    host-packed FP8 network."""
+    import torch
+
+    wl = workloads.get(name)
+    Ws, bs = wl.weights()
+    rng = np.random.default_rng(4)
+    Ws = [(np.asarray(W, np.float64) * np.exp2(rng.integers(-3, 2, size=(W.shape[0], 1)))).astype(np.float16) for W in Ws]
+    x = wl.inputs(device=device(), rows=2050)
+    expect = run(Ws, bs, x, layout=B.MLP_LAYOUT_PACKED_FP8)
+    dW, db = _device_weights(Ws, bs)
+    B.mlp_pack_weights_device([t.data_ptr() for t in dW], [t.data_ptr() for t in db], list(wl.widths),
+                              B.MLP_LAYOUT_PACKED_FP8, torch.cuda.current_stream().cuda_stream)
+    log("FP8 inference after device pack", name)
+    got = run(Ws, bs, x, layout=B.MLP_LAYOUT_PACKED_FP8, pack=False)
     assert np.array_equal(got, expect)
