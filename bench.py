@@ -433,6 +433,8 @@ def main() -> int:
     ap.add_argument("--no-variants", action="store_true", help="skip the row-major / scalarised A/B")
     ap.add_argument("--layout", choices=("packed", "rowmajor"), default="packed",
                     help="weight layout of the headline measurement (default: packed)")
+    ap.add_argument("--activation", choices=("vector", "scalarised"), default="vector",
+                    help="activation form of the headline measurement (default: vector)")
     ap.add_argument("--cpu-rows", type=int, default=65536, help="rows of the CPU-oracle sample (0: skip)")
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload table")
     ap.add_argument("--no-overlap", action="store_true", help="skip the two-stream overlap measurement")
@@ -482,8 +484,9 @@ def main() -> int:
 
     wl = workloads.get(args.workload)
     layered_net = wl.name in workloads.LAYERED  # runs layer by layer: packed FP16 only, no A/B variants
-    if layered_net and args.layout != "packed":
-        print("%s runs layer by layer, which only the packed layout serves" % wl.name, file=sys.stderr)
+    if layered_net and (args.layout != "packed" or args.activation != "vector"):
+        print("%s runs layer by layer, which only the packed layout and the vector activation serve" % wl.name,
+              file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -505,10 +508,11 @@ def main() -> int:
                     "with the queue kept busy ahead, median of 10); the page quotes ~0.0086 ms for its conversion on its own GPU"}
     layout = B.MLP_LAYOUT_PACKED if args.layout == "packed" else B.MLP_LAYOUT_ROW_MAJOR
     B.mlp_pack_weights(Ws, bs, layout, sh)
-    kernel = B.mlp_kernel_name(B.MLP_ACT_VECTOR)
+    act = B.MLP_ACT_VECTOR if args.activation == "vector" else B.MLP_ACT_SCALARISED
+    kernel = B.mlp_kernel_name(act)
 
     def step():
-        B.mlp_infer_ex(wl.batch, x.data_ptr(), y.data_ptr(), sh, B.MLP_ACT_VECTOR)
+        B.mlp_infer_ex(wl.batch, x.data_ptr(), y.data_ptr(), sh, act)
 
     for _ in range(args.warmup):
         step()
@@ -589,7 +593,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "widths": list(wl.widths), "batch": wl.batch,
                    "unique_inputs": wl.unique_rows, "replicas": wl.replicas, "layout": args.layout,
-                   "activation": "vector", "flops_per_eval": wl.flops_per_eval},
+                   "activation": args.activation, "flops_per_eval": wl.flops_per_eval},
         "frac_fp16_peak": roofline["frac"],
         "pack_ms": round(pack_ms, 4),
         "pack": pack,

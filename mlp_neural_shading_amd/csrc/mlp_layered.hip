@@ -223,10 +223,271 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #undef MLPL_STEP
 }
 
+// ---- the large tile: 256 outputs x 256 rows per workgroup -------------------------------------
+//
+// For layers whose padded output width is a multiple of 256 and whose rows are whole 16-byte chunks
+// (win equal to the padded K, rows 16-byte aligned).  Four waves in a 2 x 2 grid, each computing 128
+// outputs x 128 rows (4 x 4 MFMA tiles, 256 accumulator registers: one wave per SIMD, the
+// accumulators in AGPRs).  Both operands go through LDS, K advancing 32 per stage, two stages of LDS:
+//   - weights: the stage's 16 fragments of the image ([8 output tiles][2 K blocks], 1 KB each, in
+//     fragment order), read back with one 16-byte LDS read per lane;
+//   - rows: 256 rows x 64 bytes; chunk c (16 bytes, K = 8 c .. 8 c + 7) of row r sits at
+//     r * 64 + 16 (c ^ ((r / 4) % 4)), so the 16 lanes of a fragment read that share a K chunk hit 16
+//     different bank groups (rows 4 apart land 16 bytes apart);
+//   - every thread loads 8 chunks of 16 bytes per stage (4 of weights, 4 of rows, coalesced) two
+//     stages ahead into registers and stores them into LDS at the end of the stage before; a weight
+//     tile is read from LDS by the two waves that share its outputs, a row tile by the two that share
+//     its rows.
+// Per stage a wave reads 16 fragments from LDS (8 KB) and issues 32 MFMAs (1,024 MFMA cycles).
+namespace bigtile {
+
+constexpr int BM = 256, BN = 256, BK = 32, THREADS = 256;
+constexpr int MTW = 4, NTW = 4;       // 32 x 32 tiles per wave
+constexpr int A_STAGE = BM * BK * 2;  // 16 fragments of 1 KB
+constexpr int B_STAGE = BN * BK * 2;  // 256 rows x 64 bytes
+constexpr int STAGE = A_STAGE + B_STAGE;
+
+// TWO: K has exactly two stages (kin = 64); otherwise at least four, so the K loop below runs at least
+// once (a loop that may run zero times made the compiler park the accumulators in scratch around it).
+template <bool TWO>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void layer_gemm_big(LayerArgs p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
+
+    // Workgroup -> (row tile, output tile), output tiles fastest; XCD x = b % 8 takes a contiguous run.
+    const int n_out = p.kout / BM;
+    const int64_t n_tiles = p.row_tiles * n_out;
+    const int64_t per_xcd = (n_tiles + 7) / 8;
+    const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (t >= n_tiles)
+        return;  // whole workgroup, before any barrier
+    const int64_t rt = t / n_out;
+    const int ot = (int)(t % n_out);
+    const int64_t row0 = rt * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int g = lane >> 5, n = lane & 31;
+    const int KB = p.kin / 16;
+    const int steps = p.kin / BK;  // even: kin is a multiple of 64
+
+    // This thread's loads: weight fragment f = wave + 4 i of the stage (output tile f / 2, K block
+    // f % 2), and row group q = wave + 4 i (rows 16 q .. 16 q + 15, this lane's row 16 q + lane / 4 and
+    // its chunk slot lane % 4, holding chunk (lane % 4) ^ ((row / 4) % 4)).
+    const uint8_t *a_src = p.a + ((size_t)ot * (BM / 32) * KB) * 1024 + lane * 16;
+    const _Float16 *x_src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rl = 16 * (wave + 4 * i) + (lane >> 2);
+        const int64_t row = row0 + rl < p.rows ? row0 + rl : p.rows - 1;  // past the batch: a valid row, never stored
+        x_src[i] = (const _Float16 *)p.x + row * p.ldx + 8 * ((lane & 3) ^ ((rl >> 2) & 3));
+    }
+    // Fragment reads: weights at (f * 64 + lane) * 16; rows at row * 64 + 16 ((2 kb + g) ^ ((n / 4) % 4)).
+    const int a_rd = lane * 16 + wm * MTW * 2 * 1024;
+    const int b_rd0 = A_STAGE + (wn * NTW * 32 + n) * 64 + 16 * ((0 + g) ^ ((n >> 2) & 3));
+    const int b_rd1 = A_STAGE + (wn * NTW * 32 + n) * 64 + 16 * ((2 + g) ^ ((n >> 2) & 3));
+
+    // Staging registers of the even (E) and the odd (O) stages, named one by one: arrays indexed in
+    // unrolled loops were placed in LDS by the compiler (it promotes private arrays to LDS when the
+    // workgroup leaves room), which turned every load into a load, a wait and an LDS store.
+    uint4 Ea0, Ea1, Ea2, Ea3, Eb0, Eb1, Eb2, Eb3, Oa0, Oa1, Oa2, Oa3, Ob0, Ob1, Ob2, Ob3;
+    const _Float16 *x0 = x_src[0], *x1 = x_src[1], *x2 = x_src[2], *x3 = x_src[3];
+#define BIG_LDA(R, i, stage)                                                                                   \
+    R = *(const uint4 *)(a_src + ((size_t)((wave + 4 * (i)) >> 1) * KB + 2 * (stage) + ((wave + 4 * (i)) & 1)) * 1024)
+#define BIG_LOAD(P, stage)                                                                                     \
+    do {                                                                                                       \
+        BIG_LDA(P##a0, 0, stage);                                                                              \
+        BIG_LDA(P##a1, 1, stage);                                                                              \
+        BIG_LDA(P##a2, 2, stage);                                                                              \
+        BIG_LDA(P##a3, 3, stage);                                                                              \
+        P##b0 = *(const uint4 *)(x0 + (stage) * BK);                                                           \
+        P##b1 = *(const uint4 *)(x1 + (stage) * BK);                                                           \
+        P##b2 = *(const uint4 *)(x2 + (stage) * BK);                                                           \
+        P##b3 = *(const uint4 *)(x3 + (stage) * BK);                                                           \
+    } while (0)
+#define BIG_STORE(P, buf)                                                                                      \
+    do {                                                                                                       \
+        uint8_t *d = lds[buf] + wave * 1024 + lane * 16;                                                       \
+        *(uint4 *)(d + 0 * 4096) = P##a0;                                                                      \
+        *(uint4 *)(d + 1 * 4096) = P##a1;                                                                      \
+        *(uint4 *)(d + 2 * 4096) = P##a2;                                                                      \
+        *(uint4 *)(d + 3 * 4096) = P##a3;                                                                      \
+        *(uint4 *)(d + A_STAGE + 0 * 4096) = P##b0;                                                            \
+        *(uint4 *)(d + A_STAGE + 1 * 4096) = P##b1;                                                            \
+        *(uint4 *)(d + A_STAGE + 2 * 4096) = P##b2;                                                            \
+        *(uint4 *)(d + A_STAGE + 3 * 4096) = P##b3;                                                            \
+    } while (0)
+
+    // Accumulators start at the bias tiles (the C operand of the first MFMA).
+    f16x acc[MTW][NTW];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+        const int mtg = ot * (BM / 32) + wm * MTW + mt;
+        const f4 *bt = (const f4 *)(p.bias + mtg * 32 + g * 16);
+        const f4 b0 = bt[0], b1 = bt[1], b2 = bt[2], b3 = bt[3];
+        f16x b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            b[j] = b0[j];
+            b[4 + j] = b1[j];
+            b[8 + j] = b2[j];
+            b[12 + j] = b3[j];
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+            acc[mt][nt] = b;
+    }
+
+    // The fragments of one K block (4 of weights, 4 of rows), read together; the next block's are
+    // requested before this block's 16 MFMAs (the empty asm keeps each block's reads together: left
+    // alone the compiler reads one weight fragment at a time and each waits out the LDS latency).
+#define BIG_FRAGS(A0, A1, A2, A3, B0, B1, B2, B3, buf, kb)                                                     \
+    do {                                                                                                       \
+        const uint8_t *la = lds[buf] + a_rd + (kb) * 1024;                                                     \
+        const uint8_t *lb = lds[buf] + ((kb) ? b_rd1 : b_rd0);                                                 \
+        A0 = *(const h8 *)(la + 0 * 2048);                                                                     \
+        A1 = *(const h8 *)(la + 1 * 2048);                                                                     \
+        A2 = *(const h8 *)(la + 2 * 2048);                                                                     \
+        A3 = *(const h8 *)(la + 3 * 2048);                                                                     \
+        B0 = *(const h8 *)(lb + 0 * 2048);                                                                     \
+        B1 = *(const h8 *)(lb + 1 * 2048);                                                                     \
+        B2 = *(const h8 *)(lb + 2 * 2048);                                                                     \
+        B3 = *(const h8 *)(lb + 3 * 2048);                                                                     \
+        asm volatile("" ::"v"(A0), "v"(A1), "v"(A2), "v"(A3), "v"(B0), "v"(B1), "v"(B2), "v"(B3));             \
+    } while (0)
+#define BIG_ROW(mt, A, B0, B1, B2, B3)                                                                         \
+    do {                                                                                                       \
+        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B0, acc[mt][0], 0, 0, 0);                       \
+        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B1, acc[mt][1], 0, 0, 0);                       \
+        acc[mt][2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B2, acc[mt][2], 0, 0, 0);                       \
+        acc[mt][3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B3, acc[mt][3], 0, 0, 0);                       \
+    } while (0)
+#define BIG_MFMAS16(A0, A1, A2, A3, B0, B1, B2, B3)                                                             \
+    do {                                                                                                       \
+        BIG_ROW(0, A0, B0, B1, B2, B3);                                                                        \
+        BIG_ROW(1, A1, B0, B1, B2, B3);                                                                        \
+        BIG_ROW(2, A2, B0, B1, B2, B3);                                                                        \
+        BIG_ROW(3, A3, B0, B1, B2, B3);                                                                        \
+    } while (0)
+    h8 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3;  // K block 0 of a stage
+    h8 qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3;  // K block 1
+    // Stage s (staging set P = s % 2, LDS buffer s % 2): request stage s + 2 into P (LOAD), multiply
+    // stage s (its block 0 fragments were read at the end of the stage before), store stage s + 1
+    // (staging set Q, requested a stage ago) into the other buffer (STORE), barrier, read the next
+    // stage's block 0.  The loop body has no branch (the last two stages are peeled): branches inside it
+    // made the compiler move accumulators between AGPRs and VGPRs around them.
+#define BIG_STEP(P, Q, buf, LOAD, STORE)                                                                       \
+    do {                                                                                                       \
+        if (LOAD)                                                                                              \
+            BIG_LOAD(P, s + 2);                                                                                \
+        BIG_FRAGS(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3, buf, 1);                                             \
+        BIG_MFMAS16(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3);                                                   \
+        BIG_MFMAS16(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3);                                                   \
+        if (STORE) {                                                                                           \
+            BIG_STORE(Q, (buf) ^ 1);                                                                           \
+            __syncthreads();                                                                                   \
+            BIG_FRAGS(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, (buf) ^ 1, 0);                                   \
+        }                                                                                                      \
+    } while (0)
+
+    BIG_LOAD(E, 0);
+    BIG_LOAD(O, 1);
+    BIG_STORE(E, 0);
+    __syncthreads();
+    BIG_FRAGS(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, 0, 0);
+    int s = 0;
+    if constexpr (!TWO) {
+        do {  // stages s and s + 1, both followed by two more
+            BIG_STEP(E, O, 0, true, true);
+            ++s;
+            BIG_STEP(O, E, 1, true, true);
+            ++s;
+        } while (s + 2 < steps);
+    }
+    BIG_STEP(E, O, 0, false, true);  // stage steps - 2
+    BIG_STEP(O, E, 1, false, false);  // stage steps - 1
+
+    // Epilogue through LDS (free once every wave has finished its last stage): each wave writes its
+    // 128 outputs x 128 rows as FP16 after the rounding and the activation, 64 rows at a time, into a
+    // 16 KB region of its own (row r, outputs 8 k .. 8 k + 3 in 8-byte chunk c = 2 k' at
+    // r * 256 + 8 (c ^ (r % 32)): the 32 rows a write touches fall in 32 different bank pairs), then
+    // reads it back row by row and stores 16 bytes per lane, whole 256-byte row segments.  The writes
+    // have no condition (lane (g, n) of tile (mt, nt) holds outputs 32 mt + 8 q + 4 g + i of row
+    // 32 nt + n); only the stores check the batch and the output width, on a few registers, so the
+    // 256 accumulators stream out of the AGPRs instead of being spilled around branches.
+    __syncthreads();
+    const h4 s4 = (h4)slope();
+    uint8_t *ob = &lds[0][0] + wave * 16384;
+    const bool vec16 = p.ldy % 8 == 0 && ((uintptr_t)p.y & 15) == 0;
+#define BIG_OUT_TILE(mt, nt, u)                                                                                \
+    do {                                                                                                       \
+        const int rl = 32 * (u) + n;                                                                           \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                        \
+            const f4 part = {acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]}; \
+            h4 v = __builtin_convertvector(part, h4); /* nearest even */                                       \
+            if (p.act)                                                                                         \
+                v = __builtin_elementwise_max(v, v * s4);                                                      \
+            const int c = 8 * (mt) + 2 * q + g;                                                                \
+            *(h4 *)(ob + rl * 256 + 8 * (c ^ (rl & 31))) = v;                                                  \
+        }                                                                                                      \
+    } while (0)
+#define BIG_OUT_HALF(h)                                                                                        \
+    do {                                                                                                       \
+        _Pragma("unroll") for (int mt = 0; mt < MTW; ++mt) {                                                   \
+            BIG_OUT_TILE(mt, 2 * (h), 0);                                                                      \
+            BIG_OUT_TILE(mt, 2 * (h) + 1, 1);                                                                  \
+        }                                                                                                      \
+        const int k = lane & 15;                                                                               \
+        const int col = ot * BM + wm * MTW * 32 + 8 * k;                                                       \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                                       \
+            const int rl = 4 * i + (lane >> 4);                                                                \
+            const int64_t row = row0 + wn * NTW * 32 + 64 * (h) + rl;                                          \
+            const uint2 lo = *(const uint2 *)(ob + rl * 256 + 8 * ((2 * k) ^ (rl & 31)));                      \
+            const uint2 hi = *(const uint2 *)(ob + rl * 256 + 8 * ((2 * k + 1) ^ (rl & 31)));                  \
+            if (row < p.rows) {                                                                                \
+                _Float16 *yr = (_Float16 *)p.y + row * p.ldy + col;                                            \
+                if (vec16 && col + 8 <= p.wout) {                                                              \
+                    *(uint4 *)yr = make_uint4(lo.x, lo.y, hi.x, hi.y);                                         \
+                } else {                                                                                       \
+                    const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);                                        \
+                    const h8 v8 = __builtin_bit_cast(h8, w);                                                   \
+                    _Pragma("unroll") for (int e = 0; e < 8; ++e) if (col + e < p.wout) yr[e] = v8[e];         \
+                }                                                                                              \
+            }                                                                                                  \
+        }                                                                                                      \
+    } while (0)
+    BIG_OUT_HALF(0);
+    BIG_OUT_HALF(1);
+#undef BIG_LDA
+#undef BIG_LOAD
+#undef BIG_STORE
+#undef BIG_FRAGS
+#undef BIG_ROW
+#undef BIG_MFMAS16
+#undef BIG_STEP
+#undef BIG_OUT_TILE
+#undef BIG_OUT_HALF
+}
+
+}  // namespace bigtile
+
 }  // namespace
+
+bool layer_big_tile(const LayerArgs &p) { return p.kout % bigtile::BM == 0 && p.vec_x && p.win == p.kin; }
 
 hipError_t launch_layer(const LayerArgs &p, hipStream_t stream)
 {
+    if (layer_big_tile(p)) {
+        const int64_t tiles = ((p.rows + bigtile::BN - 1) / bigtile::BN) * (p.kout / bigtile::BM);
+        LayerArgs q = p;
+        q.row_tiles = (p.rows + bigtile::BN - 1) / bigtile::BN;
+        const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
+        if (p.kin / bigtile::BK == 2)
+            hipLaunchKernelGGL(bigtile::layer_gemm_big<true>, grid, dim3(bigtile::THREADS), 0, stream, q);
+        else
+            hipLaunchKernelGGL(bigtile::layer_gemm_big<false>, grid, dim3(bigtile::THREADS), 0, stream, q);
+        return hipGetLastError();
+    }
     const int64_t tiles = p.row_tiles * (p.kout / kBM);
     const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
     if (p.vec_x && p.win == p.kin)

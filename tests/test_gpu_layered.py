@@ -102,6 +102,59 @@ def test_permutation_chain_bit_exact(oracle_mod):
     assert np.array_equal(run(Ws, bs, x), oracle_mod.mlp_forward(Ws, bs, x))
 
 
+def _signed_chain(widths, rng, diag=(1, -64, -1, -64, -1, -64, -1, 1)):
+    Ws, bs = [], []
+    for l in range(len(widths) - 1):
+        win, wout = widths[l], widths[l + 1]
+        W = np.zeros((wout, win))
+        src = rng.permutation(max(win, wout))
+        for r in range(wout):
+            W[r, src[r] % win] = diag[l % len(diag)]
+        Ws.append(f16(W))
+        bs.append(f16(np.zeros(wout)))
+    return Ws, bs
+
+
+@pytest.mark.parametrize("rows", [517, 1000, 2048])
+def test_large_tile_layers_bit_exact(oracle_mod, rows):
+    """Layers whose padded output width is a multiple of 256 and whose input rows are whole 16-byte
+    chunks (input width = its padding to 64) run on the 256 x 256 workgroup tile, K = 64 in its
+    two-stage form: 64 -> 512 (K = 64), 512 -> 256, 256 -> 768, 768 -> 1000 (1,024 padded outputs, 1,000
+    stored), then 1000 -> 16 on the 128 x 256 tile.  Integer-exact nets (against int64 products) and
+    a signed permutation chain (against the oracle), bit for bit, over partial row tiles."""
+    widths = (64, 512, 256, 768, 1000, 16)
+    rng = np.random.default_rng(rows)
+    L = len(widths) - 1
+    W = [np.zeros((widths[l + 1], widths[l]), np.int64) for l in range(L)]
+    for l in range(L):
+        for r in range(widths[l + 1]):
+            W[l][r, rng.integers(0, widths[l], size=2 if l == 0 else 1)] += 1
+    b = [rng.integers(0, 2, size=widths[l + 1]) for l in range(L)]
+    x = rng.integers(0, 4, size=(rows, widths[0]))
+    h = x.copy()
+    for l in range(L):
+        h = h @ W[l].T + b[l]
+    assert h.max() <= 2048
+    Wf, bf, xf = [f16(w) for w in W], [f16(v) for v in b], f16(x).view(np.uint16)
+    log("integer-exact large-tile net", widths, "rows", rows)
+    assert np.array_equal(run(Wf, bf, xf), f16(h).view(np.uint16))
+    Ws, bs = _signed_chain(widths, rng)
+    xs = _x(rows, widths[0], rows + 1)
+    log("signed permutation chain, large tile", widths, "rows", rows)
+    assert np.array_equal(run(Ws, bs, xs), oracle_mod.mlp_forward(Ws, bs, xs))
+
+
+def test_large_tile_random_net(oracle_mod):
+    widths = (64, 1024, 1024, 1000, 16)
+    Ws, bs = workloads.init_weights(widths, seed=21)
+    x = _x(1333, widths[0], 21)
+    log("large-tile random net", widths)
+    y = run(Ws, bs, x)
+    ref = oracle_mod.mlp_forward(Ws, bs, x, threads=host_threads())
+    stats = compare(y, ref, what=str(widths))
+    log("  max |d| %.3g, bit-identical %.4f" % (stats["max_abs"], stats["bit_identical_frac"]))
+
+
 def test_device_conversion_of_a_layered_net():
     import torch
 
