@@ -53,6 +53,7 @@ struct State {
     int layout = MLP_LAYOUT_PACKED;
     const KernelEntry *entry[2] = {nullptr, nullptr};  // per activation form
     int grid_cap[2] = {0, 0};
+    int cus = 0;  // compute units of the device
     void *image = nullptr;
     size_t bytes = 0;
     int device = -1;
@@ -287,6 +288,7 @@ int new_state(int n_layers, const int32_t *widths, int layout, const KernelEntry
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, next.device);
     if (err != hipSuccess)
         return hip_fail(err, "hipDeviceGetAttribute(multiProcessorCount)");
+    next.cus = cus;
     for (int a = 0; a < 2; ++a) {
         const KernelEntry *k = next.entry[a];
         if (!k || is_layered(k))
@@ -520,6 +522,7 @@ int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t 
             a.act = l + 1 < L;
             a.vec_x = a.ldx % 8 == 0 && ((uintptr_t)a.x & 15) == 0;
             a.vec_y = a.ldy % 4 == 0 && ((uintptr_t)a.y & 7) == 0;
+            a.cus = g_net.cus;
             err = mlpk::launch_layer(a, stream);
         }
     }

@@ -36,6 +36,7 @@ struct LayerArgs {
     int act;            // 1: leaky ReLU after the rounding; 0: none (last layer)
     int vec_x;          // 1: rows of x are 16-byte aligned (ldx % 8 == 0, x aligned)
     int vec_y;          // 1: rows of y are 8-byte aligned (ldy % 4 == 0, y aligned)
+    int cus;            // compute units of the device (sizes the persistent grid)
 };
 
 hipError_t launch_layer(const LayerArgs &p, hipStream_t stream);

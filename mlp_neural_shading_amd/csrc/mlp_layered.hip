@@ -8,7 +8,10 @@
 // -- the same arithmetic as the fused path ("Profiling neural material inference", "Experiment
 // setup" and "Bad versus good activation"), with the activations between layers in device memory.
 //
-// Tiling (v_mfma_f32_32x32x16_f16, weights = A operand, rows = B operand, as in the fused kernel):
+// Two tilings (v_mfma_f32_32x32x16_f16, weights = A operand, rows = B operand, as in the fused
+// kernel): layers whose padded output width is a multiple of 256 and whose rows are whole 16-byte
+// chunks run on a 256 x 256 workgroup tile with both operands staged through LDS (described
+// below, before the kernel); every other layer on this 128 x 256 one:
 //   - a workgroup (4 waves) computes 128 outputs x 256 rows; each wave owns 64 rows (two 32-row
 //     sample tiles) and all 128 outputs (four output tiles), so every A fragment read from LDS feeds
 //     two MFMAs and every B fragment four;
@@ -249,7 +252,11 @@ constexpr int STAGE = A_STAGE + B_STAGE;
 
 // TWO: K has exactly two stages (kin = 64); otherwise at least four, so the K loop below runs at least
 // once (a loop that may run zero times made the compiler park the accumulators in scratch around it).
-template <bool TWO>
+// FULL: every padded output column is stored (wout = kout) and the output rows are 16-byte aligned.
+constexpr int RSRC_WORD3 = 0x00020000;  // raw buffer, 32-bit data format: range-checked byte offsets
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+template <bool TWO, bool FULL>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void layer_gemm_big(LayerArgs p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
@@ -419,6 +426,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const h4 s4 = (h4)slope();
     uint8_t *ob = &lds[0][0] + wave * 16384;
     const bool vec16 = p.ldy % 8 == 0 && ((uintptr_t)p.y & 15) == 0;
+    const int ldy2 = (int)p.ldy * 2;  // FULL only: at most 256 rows x 8 KB past the resource's base
+    const int64_t left = p.rows - row0;
+    const __amdgpu_buffer_rsrc_t out_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (_Float16 *)p.y + row0 * p.ldy, 0, (int)((left < BN ? left : BN) * p.ldy * 2), RSRC_WORD3);
 #define BIG_OUT_TILE(mt, nt, u)                                                                                \
     do {                                                                                                       \
         const int rl = 32 * (u) + n;                                                                           \
@@ -431,6 +442,20 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
             *(h4 *)(ob + rl * 256 + 8 * (c ^ (rl & 31))) = v;                                                  \
         }                                                                                                      \
     } while (0)
+// Every padded output is stored (FULL): the 16 row quads of a half go out as buffer stores against a
+// resource spanning this tile's rows within the batch, so rows past the batch fall outside it and
+// write nothing, with no branch: the LDS reads then issue back to back instead of one read, one wait
+// and one store at a time under a branch per row quad.
+#define BIG_OUT_STORES(h)                                                                                      \
+    do {                                                                                                       \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                                       \
+            const int rl = 4 * i + (lane >> 4);                                                                \
+            const uint2 lo = *(const uint2 *)(ob + rl * 256 + 8 * ((2 * k) ^ (rl & 31)));                      \
+            const uint2 hi = *(const uint2 *)(ob + rl * 256 + 8 * ((2 * k + 1) ^ (rl & 31)));                  \
+            __builtin_amdgcn_raw_buffer_store_b128(u4{lo.x, lo.y, hi.x, hi.y}, out_rs,                         \
+                                                   (wn * NTW * 32 + 64 * (h) + rl) * ldy2 + 2 * col, 0, 0);    \
+        }                                                                                                      \
+    } while (0)
 #define BIG_OUT_HALF(h)                                                                                        \
     do {                                                                                                       \
         _Pragma("unroll") for (int mt = 0; mt < MTW; ++mt) {                                                   \
@@ -439,6 +464,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
         }                                                                                                      \
         const int k = lane & 15;                                                                               \
         const int col = ot * BM + wm * MTW * 32 + 8 * k;                                                       \
+        if constexpr (FULL) {                                                                                  \
+            BIG_OUT_STORES(h);                                                                                 \
+        } else                                                                                                 \
         _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                                       \
             const int rl = 4 * i + (lane >> 4);                                                                \
             const int64_t row = row0 + wn * NTW * 32 + 64 * (h) + rl;                                          \
@@ -467,7 +495,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #undef BIG_STEP
 #undef BIG_OUT_TILE
 #undef BIG_OUT_HALF
+#undef BIG_OUT_STORES
 }
+
+
 
 }  // namespace bigtile
 
@@ -481,11 +512,12 @@ hipError_t launch_layer(const LayerArgs &p, hipStream_t stream)
         const int64_t tiles = ((p.rows + bigtile::BN - 1) / bigtile::BN) * (p.kout / bigtile::BM);
         LayerArgs q = p;
         q.row_tiles = (p.rows + bigtile::BN - 1) / bigtile::BN;
+        const int steps = p.kin / bigtile::BK;
         const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
-        if (p.kin / bigtile::BK == 2)
-            hipLaunchKernelGGL(bigtile::layer_gemm_big<true>, grid, dim3(bigtile::THREADS), 0, stream, q);
-        else
-            hipLaunchKernelGGL(bigtile::layer_gemm_big<false>, grid, dim3(bigtile::THREADS), 0, stream, q);
+        const bool full = p.wout == p.kout && p.ldy % 8 == 0 && ((uintptr_t)p.y & 15) == 0;
+        auto *k = steps == 2 ? (full ? bigtile::layer_gemm_big<true, true> : bigtile::layer_gemm_big<true, false>)
+                             : (full ? bigtile::layer_gemm_big<false, true> : bigtile::layer_gemm_big<false, false>);
+        hipLaunchKernelGGL(k, grid, dim3(bigtile::THREADS), 0, stream, q);
         return hipGetLastError();
     }
     const int64_t tiles = p.row_tiles * (p.kout / kBM);

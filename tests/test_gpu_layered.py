@@ -144,6 +144,37 @@ def test_large_tile_layers_bit_exact(oracle_mod, rows):
     assert np.array_equal(run(Ws, bs, xs), oracle_mod.mlp_forward(Ws, bs, xs))
 
 
+@pytest.mark.parametrize("rows", [700, 131849])
+def test_full_width_tiles_bit_exact(oracle_mod, rows):
+    """Layers on the 256 x 256 tile that store every padded output write their rows with range-checked
+    buffer stores, the rows past the batch falling outside the tile's range.  K depths of two, four,
+    six, eight and 32 stages (64, 128, 192, 256, 1024); 131,849 rows give up to 2,064 tiles and a
+    9-row last tile, 700 rows a 188-row one.  The 256 -> 192 layer (256 padded outputs, 192 stored)
+    takes the checked store path and 256 -> 128 and 512 -> 16 the 128 x 256 tile in between.
+    Integer-exact nets against float64 sums of small integers, and a signed permutation chain against
+    the oracle, bit for bit."""
+    widths = (64, 256, 1024, 256, 192, 256, 128, 512, 16)
+    rng = np.random.default_rng(rows)
+    L = len(widths) - 1
+    W = [np.zeros((widths[l + 1], widths[l])) for l in range(L)]
+    for l in range(L):
+        for r in range(widths[l + 1]):
+            W[l][r, rng.integers(0, widths[l], size=2 if l == 0 else 1)] += 1
+    b = [rng.integers(0, 2, size=widths[l + 1]).astype(np.float64) for l in range(L)]
+    x = rng.integers(0, 4, size=(rows, widths[0])).astype(np.float64)
+    h = x
+    for l in range(L):
+        h = h @ W[l].T + b[l]
+    assert h.max() <= 2048
+    Wf, bf, xf = [f16(w) for w in W], [f16(v) for v in b], f16(x).view(np.uint16)
+    log("integer-exact full-width net", widths, "rows", rows)
+    assert np.array_equal(run(Wf, bf, xf), f16(h).view(np.uint16))
+    Ws, bs = _signed_chain(widths, rng)
+    xs = _x(rows, widths[0], rows + 1)
+    log("signed permutation chain, full-width tiles", widths, "rows", rows)
+    assert np.array_equal(run(Ws, bs, xs), oracle_mod.mlp_forward(Ws, bs, xs, threads=host_threads()))
+
+
 def test_large_tile_random_net(oracle_mod):
     widths = (64, 1024, 1024, 1000, 16)
     Ws, bs = workloads.init_weights(widths, seed=21)
