@@ -1,12 +1,15 @@
 """Summaries of rocprofv3 output for the kernels of this library (the figures kept under profiles/).
 
-  python profile_summary.py trace KERNEL_TRACE_CSV --kernel SUBSTR [--phases 500,200,200]
+  python profile_summary.py trace KERNEL_TRACE_CSV --kernel SUBSTR [--phases 500,200,200] [--period P]
       Per-phase duration statistics of the matching dispatches, in dispatch order.  bench.py launches
       the headline kernel `--warmup` times, then `--steps` times in the timed region, then `--steps`
       times each between its own pair of events, so --phases W,K,K splits the trace the same way and
-      the middle phase is the timed region's average kernel duration.
-  python profile_summary.py counters COUNTER_CSV --kernel SUBSTR [--skip N]
-      Each counter's per-dispatch value (median, min, max) over the matching dispatches.
+      the middle phase is the timed region's average kernel duration.  With --period P every step
+      launches P kernels (one per layer of a layer-by-layer network): the phases count steps, and
+      each phase is also broken down by launch position within the step.
+  python profile_summary.py counters COUNTER_CSV --kernel SUBSTR [--skip N] [--period P]
+      Each counter's per-dispatch value (median, min, max) over the matching dispatches, the first N
+      steps skipped; with --period P (P launches per step) separately for each launch position.
   python profile_summary.py traffic --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV
           --kernel SUBSTR --workload KEY --label NAME --algorithmic-bytes B [--update]
       HBM bytes per dispatch: FETCH_SIZE and WRITE_SIZE (KiB) each scaled by what the same counter
@@ -48,7 +51,10 @@ def trace(args) -> dict:
     if not rows:
         raise SystemExit("no dispatch of a kernel matching %r in %s" % (args.kernel, args.csv))
     us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
-    phases = [int(p) for p in args.phases.split(",")] if args.phases else [len(us)]
+    period = args.period
+    if len(us) % period:
+        raise SystemExit("%d matching dispatches, not a multiple of the period %d" % (len(us), period))
+    phases = [int(p) * period for p in args.phases.split(",")] if args.phases else [len(us)]
     if sum(phases) != len(us):
         raise SystemExit("%d matching dispatches, phases add up to %d" % (len(us), sum(phases)))
     out, at = {"kernel": rows[0]["Kernel_Name"], "phases": []}, 0
@@ -65,6 +71,24 @@ def trace(args) -> dict:
         at += n
     s = out["all"]
     print("| all | %d | %.2f | %.2f | %.2f | %.2f |" % (s["n"], s["mean"], s["median"], s["min"], s["max"]))
+    if period > 1:
+        out["by_position"] = []
+        print("\n| Phase | Position | Kernel | Calls | Avg (us) | Median | Min | Max |")
+        print("|---|---|---|---|---|---|---|---|")
+        at = 0
+        for ph, n in enumerate(phases):
+            for pos in range(period):
+                sel = us[at + pos:at + n:period]
+                st = _stats(sel)
+                full = rows[at + pos]["Kernel_Name"]
+                name = full[:full.rindex("(")].split("::")[-1]  # drop the argument list and scopes
+                out["by_position"].append({"phase": ph, "position": pos, "kernel": name, **st})
+                print("| %d | %d | `%s` | %d | %.2f | %.2f | %.2f | %.2f |" % (ph, pos, name, st["n"], st["mean"], st["median"],
+                                                                      st["min"], st["max"]))
+            steps = [sum(us[at + i * period:at + (i + 1) * period]) for i in range(n // period)]
+            print("| %d | sum per step | | %d | %.2f | %.2f | %.2f | %.2f |" % (ph, len(steps), statistics.fmean(steps),
+                                                                            statistics.median(steps), min(steps), max(steps)))
+            at += n
     return out
 
 
@@ -80,14 +104,17 @@ def _per_dispatch(path, kernel, skip=0):
 
 
 def counters(args) -> dict:
-    per = _per_dispatch(args.csv, args.kernel, args.skip)
-    print("| Counter | Dispatches | Median | Min | Max |")
-    print("|---|---|---|---|---|")
+    per = _per_dispatch(args.csv, args.kernel, args.skip * args.period)
     out = {}
-    for c in sorted(per):
-        s = _stats(per[c])
-        out[c] = s
-        print("| %s | %d | %.1f | %.1f | %.1f |" % (c, s["n"], s["median"], s["min"], s["max"]))
+    for pos in range(args.period):
+        if args.period > 1:
+            print("\nlaunch position %d of %d per step:" % (pos, args.period))
+        print("| Counter | Dispatches | Median | Min | Max |")
+        print("|---|---|---|---|---|")
+        for c in sorted(per):
+            s = _stats(per[c][pos::args.period])
+            out[(c, pos) if args.period > 1 else c] = s
+            print("| %s | %d | %.1f | %.1f | %.1f |" % (c, s["n"], s["median"], s["min"], s["max"]))
     return out
 
 
@@ -202,10 +229,12 @@ def main(argv=None) -> int:
     t.add_argument("csv")
     t.add_argument("--kernel", required=True)
     t.add_argument("--phases", default="")
+    t.add_argument("--period", type=int, default=1)
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("--kernel", required=True)
     c.add_argument("--skip", type=int, default=0)
+    c.add_argument("--period", type=int, default=1)
     f = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--workload", "--label"):
         f.add_argument(a, required=True)
