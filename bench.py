@@ -262,7 +262,8 @@ def measure_overlap(torch, B, wl, x, y) -> dict:
 
 def measure_layered(torch, B, workloads) -> dict:
     """Networks beyond the fused kernels (one MFMA GEMM per layer with the fused epilogue): median of
-    10 event-timed dispatches after 3 warm-ups, FLOPs = 2 * sum w_{l-1} w_l per row."""
+    10 event-timed dispatches after 40 warm-up calls (~40 ms: the first ~10 ms after the GPU has been
+    idle run ~10 % slower while the clock ramps up), FLOPs = 2 * sum w_{l-1} w_l per row."""
     res = {}
     dev = torch.device("cuda:0")
     sh = torch.cuda.current_stream().cuda_stream
@@ -273,7 +274,7 @@ def measure_layered(torch, B, workloads) -> dict:
         y = torch.empty((rows, widths[-1]), dtype=torch.float16, device=dev)
         B.mlp_pack_weights(Ws, bs, B.MLP_LAYOUT_PACKED, sh)
         f = lambda: B.mlp_infer(rows, x.data_ptr(), y.data_ptr(), sh)
-        for _ in range(3):
+        for _ in range(40):
             f()
         ms = statistics.median(time_dispatches(torch, f, 10))
         tflops = wl.flops_per_eval * rows / (ms * 1e-3) / 1e12

@@ -116,6 +116,10 @@ int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const 
  *   d_biases  n_layers host-memory entries, each a device pointer to [widths[l+1]] FP16
  *   stream    hipStream_t (NULL = the default stream) the conversion is enqueued on
  * Stream-ordered: the call allocates the image, enqueues the conversion and returns without waiting.
+ * When the current network's image has the same size on the same device and n_layers <= 8, the
+ * conversion rewrites that image in place instead (no allocation, no free, nothing that waits for the
+ * device): work already enqueued on `stream` still sees the previous network, and no mlp_infer on
+ * another stream may be running on it (as for any re-pack).
  * The weights must stay valid, and unchanged, until the stream has run the conversion; an
  * mlp_infer on the same stream sees the converted image, one on another stream must first wait for
  * this stream (e.g. with an event).  Ownership, threading and errors as for mlp_pack_weights, except

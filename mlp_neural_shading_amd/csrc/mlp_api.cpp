@@ -272,7 +272,10 @@ int mlp_pack_host(int n_layers, const int32_t *widths, const uint16_t *const *we
 namespace {
 
 // A new State for (shape, layout) served by `e`, with its device image allocated (contents unset).
-int new_state(int n_layers, const int32_t *widths, int layout, const KernelEntry *e, State &next)
+// reuse_image: take the current network's image instead when it has the same size on the same device
+// (the caller then rewrites it in place, in stream order, with no allocation and no free).
+int new_state(int n_layers, const int32_t *widths, int layout, const KernelEntry *e, State &next,
+              bool reuse_image = false)
 {
     next.n_layers = n_layers;
     for (int i = 0; i <= n_layers; ++i)
@@ -301,6 +304,10 @@ int new_state(int n_layers, const int32_t *widths, int layout, const KernelEntry
             return fail(MLP_ERR_UNSUPPORTED, "kernel %s cannot be resident on this device", k->name);
         next.grid_cap[a] = blocks * cus;
     }
+    if (reuse_image && g_net.packed && g_net.device == next.device && g_net.bytes == next.bytes) {
+        next.image = g_net.image;
+        return MLP_OK;
+    }
     err = hipMalloc(&next.image, next.bytes);
     if (err != hipSuccess) {
         next.image = nullptr;
@@ -313,7 +320,7 @@ int new_state(int n_layers, const int32_t *widths, int layout, const KernelEntry
 void commit_state(State &next)
 {
     next.packed = true;
-    if (g_net.packed)
+    if (g_net.packed && g_net.image != next.image)
         (void)hipFree(g_net.image);
     g_net = next;
 }
@@ -400,8 +407,12 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
     for (int l = 0; l < n_layers; ++l)
         if (((uintptr_t)d_weights[l] | (uintptr_t)d_biases[l]) & 1)
             return fail(MLP_ERR_INVALID_ARGUMENT, "d_weights[%d] or d_biases[%d] is not 2-byte aligned", l, l);
+    // One launch (at most 8 layers) rewrites an image of unchanged size in place: hipFree would wait for
+    // the whole device, and a conversion recorded into the stream should not.  Deeper networks take
+    // several launches and a new image, so a failed launch never leaves the current network half
+    // rewritten.
     State next;
-    rc = new_state(n_layers, widths, layout, e, next);
+    rc = new_state(n_layers, widths, layout, e, next, n_layers <= 8);
     if (rc != MLP_OK)
         return rc;
     // The conversion kernel takes up to 8 layers per launch.
@@ -419,7 +430,8 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
         args.dst = (uint8_t *)next.image;
         const hipError_t err = mlpk::launch_pack(args, count, (hipStream_t)stream);
         if (err != hipSuccess) {
-            (void)hipFree(next.image);
+            if (next.image != g_net.image)
+                (void)hipFree(next.image);
             return hip_fail(err, "launching the device packer");
         }
     }

@@ -102,3 +102,32 @@ def test_fp8_inference_after_device_pack(name):
     log("FP8 inference after device pack", name)
     got = run(Ws, bs, x, layout=B.MLP_LAYOUT_PACKED_FP8, pack=False)
     assert np.array_equal(got, expect)
+
+
+def test_repack_in_place_is_stream_ordered():
+    """A device conversion of a network whose image has the size of the current one rewrites that image
+    in place, in stream order: the inference enqueued before it on the same stream still computes the
+    first network, the one after it the second, with no host synchronisation in between."""
+    import torch
+
+    wl = workloads.get("page")
+    Ws1, bs1 = wl.weights()
+    Ws2, bs2 = workloads.init_weights(list(wl.widths), seed=77)
+    x = wl.inputs(device=device(), rows=4133)
+    expect1, expect2 = run(Ws1, bs1, x), run(Ws2, bs2, x)
+    assert not np.array_equal(expect1, expect2)
+    dW1, db1 = _device_weights(Ws1, bs1)
+    dW2, db2 = _device_weights(Ws2, bs2)
+    stream = torch.cuda.current_stream().cuda_stream
+    outs = [torch.full((x.shape[0], wl.widths[-1]), float("nan"), dtype=torch.float16, device=device())
+            for _ in range(3)]
+    log("in-place re-pack, page net, 3 conversions and inferences on one stream")
+    for (dW, db), out in zip([(dW1, db1), (dW2, db2), (dW1, db1)], outs):
+        B.mlp_pack_weights_device([t.data_ptr() for t in dW], [t.data_ptr() for t in db], list(wl.widths),
+                                  B.MLP_LAYOUT_PACKED, stream)
+        B.mlp_infer(x.shape[0], x.data_ptr(), out.data_ptr(), stream)
+    torch.cuda.synchronize()
+    got = [o.cpu().view(torch.int16).numpy().view(np.uint16) for o in outs]
+    assert np.array_equal(got[0], expect1)
+    assert np.array_equal(got[1], expect2)
+    assert np.array_equal(got[2], expect1)
