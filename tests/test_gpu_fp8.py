@@ -9,8 +9,9 @@ C ABI, on the dedicated shapes.
     pre-activation through the binary16 leaky slope;
   - the eight-layer sign-alternating diagonal golden (tests/golden/fp8_sign_alternating_diag.json),
     embedded in the small shape;
-- random weights at the workloads' initialisations, ragged row counts: the contract tolerance on every
-  element and the FP8 bar below.
+- random weights at the workloads' initialisations, ragged row counts, and at full size on sampled rows
+  in the benchmark's launch configuration: the contract tolerance on every element and the FP8 bar
+  below.
 
 The FP8 bar (its own tolerance: the contract's 1e-2 is stated for the FP16 network).  The kernel and
 the oracle quantise identically (the same E4M3 codes for the weights, the same scale per row, the same
@@ -91,11 +92,21 @@ def _stats(a_bits, o_bits):
     return d, beyond
 
 
-def _compare_fp8(g_bits, o_bits, Ws, bs, x_bits, what):
-    """GPU vs oracle against the bar of the accumulator error model (module docstring)."""
+def _compare_fp8(g_bits, o_bits, Ws, bs, x_bits, what, order_free=True):
+    """GPU vs oracle against the bar of the accumulator error model (module docstring).  order_free:
+    require every sum to be exact in binary32 (then the exact-sum network gives the oracle's bits); over
+    many rows a few sums of products spanning more than 24 bits are not, and their binary32 summation
+    order matters by ~2^-24 relative, far inside the model's 2^-11 perturbation: with order_free=False
+    those outputs are counted and bounded instead."""
     g = np.asarray(g_bits).view(np.float16).astype(np.float64)
     assert np.isfinite(g).all(), what
-    assert np.array_equal(_fp8_net(Ws, bs, x_bits), o_bits), "%s: the sums are not order-free here" % what
+    exact = _fp8_net(Ws, bs, x_bits)
+    if order_free:
+        assert np.array_equal(exact, o_bits), "%s: the sums are not order-free here" % what
+    else:
+        differ = int((exact != np.asarray(o_bits)).sum())
+        log("  %s: %d of %d outputs where binary32 summation order matters" % (what, differ, exact.size))
+        assert differ <= 1e-3 * exact.size, what
     model = [_stats(_fp8_net(Ws, bs, x_bits, np.random.default_rng(100 + k), 2.0 ** -11), o_bits) for k in range(2)]
     m_max = max(d.max() for d, _ in model)
     m_mean = max(d.mean() for d, _ in model)
@@ -210,3 +221,49 @@ def test_prefixes_and_determinism(oracle_mod):
     for n in (1, 31, 33, 65, 1000):
         assert np.array_equal(run(Ws, bs, xt[:n], layout=FP8, pack=False), full[:n]), n
     assert np.array_equal(run(Ws, bs, xt, layout=FP8, pack=False), full)
+
+
+def _rows_bits(t, idx):
+    import torch
+
+    sel = t.index_select(0, torch.as_tensor(idx, device=t.device))
+    return sel.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+# Full size, one dispatch over the whole batch (the launch configuration bench.py times): every row of
+# the small net, the page net's 65,536 distinct inputs (and its 16 replicas bit-identical), and for the
+# larger nets the first and last rows plus seeded random rows (for the streaming net also the rows whose
+# inputs straddle each 2 GiB boundary), against the FP8 oracle with the bar above.
+@pytest.mark.parametrize("name,edge,n_random", [("small", 4096, 0), ("page", 65536, 0), ("hetero", 16384, 32768),
+                                                ("wide", 8192, 16384), ("stream", 8192, 16384)])
+def test_full_size_sampled(oracle_mod, name, edge, n_random):
+    import torch
+
+    wl = workloads.get(name)
+    Ws, bs = wl.weights()
+    x = wl.inputs(device="cuda")
+    y = torch.empty((wl.batch, wl.widths[-1]), dtype=torch.float16, device="cuda")
+    log("FP8 full size", wl.name)
+    B.mlp_pack_weights(Ws, bs, FP8)
+    B.mlp_infer(wl.batch, x.data_ptr(), y.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    if wl.replicas > 1:
+        u = wl.unique_rows
+        for r in range(1, wl.replicas):
+            assert torch.equal(y[r * u:(r + 1) * u], y[:u]), "replica %d differs" % r
+    rng = np.random.default_rng(78)
+    extra = []
+    if name == "stream":
+        row_bytes = 2 * wl.widths[0]
+        for k in (1, 2, 3):
+            r = (k << 31) // row_bytes
+            extra += list(range(r - 64, r + 64))
+    idx = np.concatenate([np.arange(edge), np.arange(wl.batch - edge, wl.batch),
+                          rng.integers(0, wl.batch, size=n_random), np.asarray(extra, dtype=np.int64)])
+    idx = np.unique(idx[(idx >= 0) & (idx < wl.batch)])
+    xb, yb = _rows_bits(x, idx), _rows_bits(y, idx)
+    del x, y
+    torch.cuda.empty_cache()
+    ref = oracle_mod.mlp_forward_fp8(Ws, bs, xb, threads=host_threads())
+    _compare_fp8(yb, ref, Ws, bs, xb, "%s full size (%d rows checked)" % (name, idx.size), order_free=False)

@@ -119,10 +119,11 @@ def _signed_chain(widths, rng, diag=(1, -64, -1, -64, -1, -64, -1, 1)):
 def test_large_tile_layers_bit_exact(oracle_mod, rows):
     """Layers whose padded output width is a multiple of 256 and whose input rows are whole 16-byte
     chunks (input width = its padding to 64) run on the 256 x 256 workgroup tile, K = 64 in its
-    two-stage form: 64 -> 512 (K = 64), 512 -> 256, 256 -> 768, 768 -> 1000 (1,024 padded outputs, 1,000
-    stored), then 1000 -> 16 on the 128 x 256 tile.  Integer-exact nets (against int64 products) and
-    a signed permutation chain (against the oracle), bit for bit, over partial row tiles."""
-    widths = (64, 512, 256, 768, 1000, 16)
+    two-stage form: 64 -> 512 (K = 64), 512 -> 256, 256 -> 768, 768 -> 1024, 1024 -> 1000 (K of 32
+    stages, split around the barrier; 1,024 padded outputs, 1,000 stored), then 1000 -> 16 on the
+    128 x 256 tile.  Integer-exact nets (against int64 products) and a signed permutation chain
+    (against the oracle), bit for bit, over partial row tiles."""
+    widths = (64, 512, 256, 768, 1024, 1000, 16)
     rng = np.random.default_rng(rows)
     L = len(widths) - 1
     W = [np.zeros((widths[l + 1], widths[l]), np.int64) for l in range(L)]
@@ -131,9 +132,9 @@ def test_large_tile_layers_bit_exact(oracle_mod, rows):
             W[l][r, rng.integers(0, widths[l], size=2 if l == 0 else 1)] += 1
     b = [rng.integers(0, 2, size=widths[l + 1]) for l in range(L)]
     x = rng.integers(0, 4, size=(rows, widths[0]))
-    h = x.copy()
+    h = x.astype(np.float64)  # sums of small integers: exact in float64, and BLAS-fast
     for l in range(L):
-        h = h @ W[l].T + b[l]
+        h = h @ W[l].T.astype(np.float64) + b[l]
     assert h.max() <= 2048
     Wf, bf, xf = [f16(w) for w in W], [f16(v) for v in b], f16(x).view(np.uint16)
     log("integer-exact large-tile net", widths, "rows", rows)
