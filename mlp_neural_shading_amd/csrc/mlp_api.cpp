@@ -516,12 +516,44 @@ int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t 
     hipError_t err = hipSuccess;
     for (int64_t r0 = 0; r0 < batch && err == hipSuccess; r0 += chunk) {
         const int64_t rows = batch - r0 < chunk ? batch - r0 : chunk;
-        for (int l = 0; l < L && err == hipSuccess; ++l) {
+        // layer j's input and output rows in this block
+        auto x_of = [&](int j) { return j == 0 ? (const uint16_t *)in_ptr + r0 * w[0] : (const uint16_t *)buf[(j - 1) & 1]; };
+        auto ldx_of = [&](int j) { return (int64_t)(j == 0 ? w[0] : ld_max); };
+        auto y_of = [&](int j) { return j == L - 1 ? (uint16_t *)out_ptr + r0 * w[L] : (uint16_t *)buf[j & 1]; };
+        auto ldy_of = [&](int j) { return (int64_t)(j == L - 1 ? w[L] : ld_max); };
+        for (int l = 0; l < L && err == hipSuccess;) {
+            // A chain [l, e): layers of 256 padded outputs and K 128..256, the first reading whole
+            // 16-byte rows of exactly its K columns, the last writing 16-byte rows of 256 outputs.
+            int e = l;
+            while (e < L && e - l < mlpk::kChainMaxLayers && mlpk::layered_chainable(w[e], w[e + 1]))
+                ++e;
+            while (e - l >= 2 && !(w[e] == mlpk::kChainWidth && ldy_of(e - 1) % 8 == 0 && ((uintptr_t)y_of(e - 1) & 15) == 0))
+                --e;
+            const bool whole_x = w[l] == mlpk::layered_kin(w[l]) && ldx_of(l) % 8 == 0 && ((uintptr_t)x_of(l) & 15) == 0;
+            if (e - l >= 2 && whole_x) {
+                mlpk::ChainArgs c{};
+                c.x = x_of(l);
+                c.ldx = ldx_of(l);
+                c.y = y_of(e - 1);
+                c.ldy = ldy_of(e - 1);
+                c.image = (const uint8_t *)g_net.image;
+                c.rows = rows;
+                c.row_tiles = (rows + mlpk::kChainWidth - 1) / mlpk::kChainWidth;
+                c.n = e - l;
+                c.act_last = e < L;
+                for (int j = l; j < e; ++j) {
+                    c.off[j - l] = mlpk::layered_layer_offset(w, j);
+                    c.kin[j - l] = mlpk::layered_kin(w[j]);
+                }
+                err = mlpk::launch_chain(c, stream);
+                l = e;
+                continue;
+            }
             mlpk::LayerArgs a{};
-            a.x = l == 0 ? (const uint16_t *)in_ptr + r0 * w[0] : (const uint16_t *)buf[(l - 1) & 1];
-            a.ldx = l == 0 ? w[0] : ld_max;
-            a.y = l == L - 1 ? (uint16_t *)out_ptr + r0 * w[L] : (uint16_t *)buf[l & 1];
-            a.ldy = l == L - 1 ? w[L] : ld_max;
+            a.x = x_of(l);
+            a.ldx = ldx_of(l);
+            a.y = y_of(l);
+            a.ldy = ldy_of(l);
             const size_t off = mlpk::layered_layer_offset(w, l);
             a.a = (const uint8_t *)g_net.image + off;
             a.bias = (const float *)((const uint8_t *)g_net.image + off + mlpk::layered_a_bytes(w[l], w[l + 1]));
@@ -536,6 +568,7 @@ int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t 
             a.vec_y = a.ldy % 4 == 0 && ((uintptr_t)a.y & 7) == 0;
             a.cus = g_net.cus;
             err = mlpk::launch_layer(a, stream);
+            ++l;
         }
     }
     if (!ext)

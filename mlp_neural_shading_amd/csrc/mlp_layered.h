@@ -41,6 +41,33 @@ struct LayerArgs {
 
 hipError_t launch_layer(const LayerArgs &p, hipStream_t stream);
 
+// A run of consecutive layers whose padded output width is 256 and whose K is 128..256, in one launch:
+// each workgroup keeps its 256 rows' activations in LDS from the first layer's input to the last
+// layer's output, so only the chain's input and output pass through device memory.
+constexpr int kChainMaxLayers = 64;
+constexpr int kChainWidth = 256;
+struct ChainArgs {
+    const uint16_t *x;  // [rows][ldx] FP16: the first layer's input, kin[0] columns, rows 16-byte aligned
+    int64_t ldx;
+    uint16_t *y;        // [rows][ldy] FP16: the last layer's 256 outputs, rows 16-byte aligned (may be x)
+    int64_t ldy;
+    const uint8_t *image;  // the layered weight image
+    int64_t rows;
+    int64_t row_tiles;     // ceil(rows / 256)
+    int n;                 // layers in the chain, 2 .. kChainMaxLayers
+    int act_last;          // 1: leaky ReLU after the chain's last layer too
+    uint64_t off[kChainMaxLayers];  // byte offset of each layer's A fragments in the image
+    int kin[kChainMaxLayers];       // each layer's padded K: 128, 192 or 256
+};
+
+// Whether layer l (real widths win -> wout) can sit in a chain (its input then comes from LDS).
+inline bool layered_chainable(int win, int wout)
+{
+    return layered_kout(wout) == kChainWidth && layered_kin(win) >= 128 && layered_kin(win) <= kChainWidth;
+}
+
+hipError_t launch_chain(const ChainArgs &c, hipStream_t stream);
+
 // Rows one workgroup covers (the row tile).
 int layered_rows_per_tile();
 

@@ -560,6 +560,191 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 
 
 
+
+// ---- a chain of 256-wide layers: the row tile's activations stay in LDS ---------------------------
+//
+// For consecutive layers with 256 padded outputs and K of 128..256 (every layer of a 256-wide net),
+// one workgroup (the 2 x 2 waves of the tile above, 256 accumulators each in AGPRs) takes 256 rows
+// through all the chain's layers.  Its activations live in a 128 KB LDS tile (row r's 16-byte chunk k,
+// features 8 k .. 8 k + 7, at r * 512 + 16 (k ^ (r % 32)): the 32 rows of a fragment read or an
+// epilogue write hit 32 different chunk slots), which the first layer's input rows are copied into
+// and the last layer's outputs are copied out of; only the weights stream in, through two 16 KB
+// stages per 32-deep K step, as in the tile above.  A layer's epilogue (nearest-even rounding, the
+// leaky ReLU) writes its outputs back into the tile, where the padded outputs (zero weights and bias)
+// are exact zeros for the next layer's padded K.  Device-memory traffic per chain: its input and its
+// output, instead of every layer's, which makes a 256-wide net bound by the MFMA pipe instead of HBM.
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void layer_chain(ChainArgs c)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t act[BN * 512];
+    __shared__ __attribute__((aligned(16))) uint8_t ast[2][A_STAGE];
+
+    const int64_t rt = blockIdx.x;
+    if (rt >= c.row_tiles)
+        return;  // whole workgroup, before any barrier
+    const int64_t row0 = rt * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int g = lane >> 5, n = lane & 31;
+
+    // The first layer's input: 16-byte chunks of the tile's rows (rows past the batch repeat the last
+    // row; their outputs are never stored).
+    {
+        const int kc = c.kin[0] / 8;
+        for (int i = tid; i < BN * kc; i += THREADS) {
+            const int r = i / kc, k = i - r * kc;
+            const int64_t row = row0 + r < c.rows ? row0 + r : c.rows - 1;
+            const uint4 v = *(const uint4 *)(c.x + row * c.ldx + 8 * k);
+            *(uint4 *)(act + r * 512 + 16 * (k ^ (r & 31))) = v;
+        }
+    }
+
+    const h4 s4 = (h4)slope();
+    // B fragment rows of this lane: tile nt's row wn * 128 + 32 nt + n, whose chunk k sits at
+    // row * 512 + 16 (k ^ n).
+    const int b_row = (wn * NTW * 32 + n) * 512;
+    const int a_rd = lane * 16 + wm * MTW * 2 * 1024;
+    uint4 Ea0, Ea1, Ea2, Ea3, Oa0, Oa1, Oa2, Oa3;
+    h8 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3;
+    h8 qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3;
+    f16x acc[MTW][NTW];
+
+    for (int l = 0; l < c.n; ++l) {
+        const uint8_t *A = c.image + c.off[l];
+        const int KB = c.kin[l] / 16;
+        const int steps = c.kin[l] / BK;  // 4, 6 or 8
+        const uint8_t *a_src = A + lane * 16;
+        const f4 *bias = (const f4 *)(A + (size_t)c.kin[l] * 512);  // after the 8 x KB fragments
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt) {
+            const f4 *bt = bias + (wm * MTW + mt) * 8 + g * 4;
+            const f4 b0 = bt[0], b1 = bt[1], b2 = bt[2], b3 = bt[3];
+            f16x b;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                b[j] = b0[j];
+                b[4 + j] = b1[j];
+                b[8 + j] = b2[j];
+                b[12 + j] = b3[j];
+            }
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+                acc[mt][nt] = b;
+        }
+#define CH_LDA(R, i, stage)                                                                                    \
+    R = *(const uint4 *)(a_src + ((size_t)((wave + 4 * (i)) >> 1) * KB + 2 * (stage) + ((wave + 4 * (i)) & 1)) * 1024)
+#define CH_LOAD(P, stage)                                                                                      \
+    do {                                                                                                       \
+        CH_LDA(P##a0, 0, stage);                                                                               \
+        CH_LDA(P##a1, 1, stage);                                                                               \
+        CH_LDA(P##a2, 2, stage);                                                                               \
+        CH_LDA(P##a3, 3, stage);                                                                               \
+    } while (0)
+#define CH_STORE(P, buf)                                                                                       \
+    do {                                                                                                       \
+        uint8_t *d = ast[buf] + wave * 1024 + lane * 16;                                                       \
+        *(uint4 *)(d + 0 * 4096) = P##a0;                                                                      \
+        *(uint4 *)(d + 1 * 4096) = P##a1;                                                                      \
+        *(uint4 *)(d + 2 * 4096) = P##a2;                                                                      \
+        *(uint4 *)(d + 3 * 4096) = P##a3;                                                                      \
+    } while (0)
+// K block kbg of the layer (16 features): weight fragments from stage buffer buf (its block kbg % 2),
+// row fragments from the activation tile; read together and waited for (see BIG_FRAGS).
+#define CH_FRAGS(A0, A1, A2, A3, B0, B1, B2, B3, buf, kbg)                                                     \
+    do {                                                                                                       \
+        const uint8_t *la = ast[buf] + a_rd + ((kbg) & 1) * 1024;                                              \
+        const uint8_t *lb = act + b_row + 16 * ((2 * (kbg) + g) ^ n);                                          \
+        A0 = *(const h8 *)(la + 0 * 2048);                                                                     \
+        A1 = *(const h8 *)(la + 1 * 2048);                                                                     \
+        A2 = *(const h8 *)(la + 2 * 2048);                                                                     \
+        A3 = *(const h8 *)(la + 3 * 2048);                                                                     \
+        B0 = *(const h8 *)(lb + 0 * 32 * 512);                                                                 \
+        B1 = *(const h8 *)(lb + 1 * 32 * 512);                                                                 \
+        B2 = *(const h8 *)(lb + 2 * 32 * 512);                                                                 \
+        B3 = *(const h8 *)(lb + 3 * 32 * 512);                                                                 \
+        asm volatile("" ::"v"(A0), "v"(A1), "v"(A2), "v"(A3), "v"(B0), "v"(B1), "v"(B2), "v"(B3));             \
+    } while (0)
+#define CH_ROW(mt, A, B0, B1, B2, B3)                                                                          \
+    do {                                                                                                       \
+        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B0, acc[mt][0], 0, 0, 0);                       \
+        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B1, acc[mt][1], 0, 0, 0);                       \
+        acc[mt][2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B2, acc[mt][2], 0, 0, 0);                       \
+        acc[mt][3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B3, acc[mt][3], 0, 0, 0);                       \
+    } while (0)
+#define CH_MFMAS16(A0, A1, A2, A3, B0, B1, B2, B3)                                                             \
+    do {                                                                                                       \
+        CH_ROW(0, A0, B0, B1, B2, B3);                                                                         \
+        CH_ROW(1, A1, B0, B1, B2, B3);                                                                         \
+        CH_ROW(2, A2, B0, B1, B2, B3);                                                                         \
+        CH_ROW(3, A3, B0, B1, B2, B3);                                                                         \
+    } while (0)
+// Stage s as in the tile above (staging set P, stage buffer buf = s % 2).
+#define CH_STEP(P, Q, buf, LOAD, STORE)                                                                        \
+    do {                                                                                                       \
+        if (LOAD)                                                                                              \
+            CH_LOAD(P, s + 2);                                                                                 \
+        CH_FRAGS(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3, buf, 2 * s + 1);                                      \
+        CH_MFMAS16(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3);                                                    \
+        CH_MFMAS16(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3);                                                    \
+        if (STORE) {                                                                                           \
+            CH_STORE(Q, (buf) ^ 1);                                                                            \
+            __syncthreads();                                                                                   \
+            CH_FRAGS(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, (buf) ^ 1, 2 * s + 2);                            \
+        }                                                                                                      \
+    } while (0)
+        CH_LOAD(E, 0);
+        CH_LOAD(O, 1);
+        __syncthreads();  // the tile holds this layer's input; every wave is done with the stages
+        CH_STORE(E, 0);
+        __syncthreads();
+        CH_FRAGS(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, 0, 0);
+        int s = 0;
+        do {  // stages s and s + 1, both followed by two more
+            CH_STEP(E, O, 0, true, true);
+            ++s;
+            CH_STEP(O, E, 1, true, true);
+            ++s;
+        } while (s + 2 < steps);
+        CH_STEP(E, O, 0, false, true);
+        ++s;
+        CH_STEP(O, E, 1, false, false);
+        __syncthreads();  // every wave has read its row fragments of this layer
+
+        // Epilogue into the tile: lane (g, n) of tile (mt, nt) holds outputs 32 mt + 8 q + 4 g + i of
+        // row 32 nt + n (within the wave's quarter): features 8 k + 4 g .. + 3 of chunk
+        // k = 16 wm + 4 mt + q.
+        const bool act_l = l + 1 < c.n || c.act_last;
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f4 part = {acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2],
+                                     acc[mt][nt][4 * q + 3]};
+                    h4 v = __builtin_convertvector(part, h4);  // nearest even
+                    if (act_l)
+                        v = __builtin_elementwise_max(v, v * s4);
+                    const int k = 16 * wm + 4 * mt + q;
+                    *(h4 *)(act + b_row + nt * 32 * 512 + 16 * (k ^ n) + 8 * g) = v;
+                }
+#undef CH_LDA
+#undef CH_LOAD
+#undef CH_STORE
+#undef CH_FRAGS
+#undef CH_ROW
+#undef CH_MFMAS16
+#undef CH_STEP
+    }
+    __syncthreads();
+
+    // The last layer's outputs: 32 chunks of 16 bytes per row, rows within the batch.
+    for (int i = tid; i < BN * 32; i += THREADS) {
+        const int r = i >> 5, k = i & 31;
+        if (row0 + r < c.rows)
+            *(uint4 *)(c.y + (row0 + r) * c.ldy + 8 * k) = *(const uint4 *)(act + r * 512 + 16 * (k ^ (r & 31)));
+    }
+}
+
 }  // namespace bigtile
 
 }  // namespace
@@ -588,6 +773,12 @@ hipError_t launch_layer(const LayerArgs &p, hipStream_t stream)
         hipLaunchKernelGGL(layer_gemm<true>, grid, dim3(kThreads), 0, stream, p);
     else
         hipLaunchKernelGGL(layer_gemm<false>, grid, dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_chain(const ChainArgs &c, hipStream_t stream)
+{
+    hipLaunchKernelGGL(bigtile::layer_chain, dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
     return hipGetLastError();
 }
 

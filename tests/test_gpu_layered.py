@@ -176,6 +176,36 @@ def test_full_width_tiles_bit_exact(oracle_mod, rows):
     assert np.array_equal(run(Ws, bs, xs), oracle_mod.mlp_forward(Ws, bs, xs, threads=host_threads()))
 
 
+@pytest.mark.parametrize("widths", [(128, 256, 256, 200, 256, 256), (64, 256, 256, 256, 100), (256,) * 17])
+@pytest.mark.parametrize("rows", [517, 131849])
+def test_chained_layers_bit_exact(oracle_mod, widths, rows):
+    """Consecutive layers with 256 padded outputs and K of 128..256 run as one chain, the row tile's
+    activations kept in LDS: a whole net ending in a chain (K of 128, a 200-wide layer whose padded
+    outputs must be exact zeros for the next K, no activation after the last layer), a chain between
+    single layers (its last layer activated), and 16 layers of 256.  Integer-exact nets against
+    float64 sums of small integers, and a signed permutation chain against the oracle, bit for bit,
+    over a ragged last tile and many tiles."""
+    rng = np.random.default_rng(rows + len(widths))
+    L = len(widths) - 1
+    W = [np.zeros((widths[l + 1], widths[l])) for l in range(L)]
+    for l in range(L):
+        for r in range(widths[l + 1]):
+            W[l][r, rng.integers(0, widths[l], size=2 if l == 0 else 1)] += 1
+    b = [rng.integers(0, 2, size=widths[l + 1]).astype(np.float64) for l in range(L)]
+    x = rng.integers(0, 4, size=(rows, widths[0])).astype(np.float64)
+    h = x
+    for l in range(L):
+        h = h @ W[l].T + b[l]
+    assert h.max() <= 2048
+    Wf, bf, xf = [f16(w) for w in W], [f16(v) for v in b], f16(x).view(np.uint16)
+    log("integer-exact chained net", widths[:6], "layers", L, "rows", rows)
+    assert np.array_equal(run(Wf, bf, xf), f16(h).view(np.uint16))
+    Ws, bs = _signed_chain(widths, rng)
+    xs = _x(rows, widths[0], rows + 2)
+    log("signed permutation chain, chained layers", widths[:6], "rows", rows)
+    assert np.array_equal(run(Ws, bs, xs), oracle_mod.mlp_forward(Ws, bs, xs, threads=host_threads()))
+
+
 def test_large_tile_random_net(oracle_mod):
     widths = (64, 1024, 1024, 1000, 16)
     Ws, bs = workloads.init_weights(widths, seed=21)
