@@ -608,30 +608,15 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
     h8 qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3;
     f16x acc[MTW][NTW];
 
-    for (int l = 0; l < c.n; ++l) {
-        const uint8_t *A = c.image + c.off[l];
-        const int KB = c.kin[l] / 16;
-        const int steps = c.kin[l] / BK;  // 4, 6 or 8
-        const uint8_t *a_src = A + lane * 16;
-        const f4 *bias = (const f4 *)(A + (size_t)c.kin[l] * 512);  // after the 8 x KB fragments
-#pragma unroll
-        for (int mt = 0; mt < MTW; ++mt) {
-            const f4 *bt = bias + (wm * MTW + mt) * 8 + g * 4;
-            const f4 b0 = bt[0], b1 = bt[1], b2 = bt[2], b3 = bt[3];
-            f16x b;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                b[j] = b0[j];
-                b[4 + j] = b1[j];
-                b[8 + j] = b2[j];
-                b[12 + j] = b3[j];
-            }
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-                acc[mt][nt] = b;
-        }
+    // Weight stages: a_src / KB describe the layer being computed; its first two stages are loaded
+    // before it starts (for layer 0 here, for the others during the last two K steps of the layer
+    // before, into the staging registers those steps no longer use).
+    const uint8_t *a_src = c.image + c.off[0] + lane * 16;
+    int KB = c.kin[0] / 16;
 #define CH_LDA(R, i, stage)                                                                                    \
     R = *(const uint4 *)(a_src + ((size_t)((wave + 4 * (i)) >> 1) * KB + 2 * (stage) + ((wave + 4 * (i)) & 1)) * 1024)
+#define CH_LDN(R, i, stage)                                                                                    \
+    R = *(const uint4 *)(a_nx + ((size_t)((wave + 4 * (i)) >> 1) * KB_nx + 2 * (stage) + ((wave + 4 * (i)) & 1)) * 1024)
 #define CH_LOAD(P, stage)                                                                                      \
     do {                                                                                                       \
         CH_LDA(P##a0, 0, stage);                                                                               \
@@ -691,8 +676,33 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
             CH_FRAGS(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, (buf) ^ 1, 2 * s + 2);                            \
         }                                                                                                      \
     } while (0)
-        CH_LOAD(E, 0);
-        CH_LOAD(O, 1);
+    CH_LOAD(E, 0);
+    CH_LOAD(O, 1);
+
+    for (int l = 0; l < c.n; ++l) {
+        const uint8_t *A = c.image + c.off[l];
+        const int steps = KB / 2;  // 4, 6 or 8
+        // the next layer's weights (the last layer reloads its own, unused: no branch)
+        const int ln = l + 1 < c.n ? l + 1 : l;
+        const uint8_t *a_nx = c.image + c.off[ln] + lane * 16;
+        const int KB_nx = c.kin[ln] / 16;
+        const f4 *bias = (const f4 *)(A + (size_t)KB * 16 * 512);  // after the 8 x KB fragments
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt) {
+            const f4 *bt = bias + (wm * MTW + mt) * 8 + g * 4;
+            const f4 b0 = bt[0], b1 = bt[1], b2 = bt[2], b3 = bt[3];
+            f16x b;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                b[j] = b0[j];
+                b[4 + j] = b1[j];
+                b[8 + j] = b2[j];
+                b[12 + j] = b3[j];
+            }
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+                acc[mt][nt] = b;
+        }
         __syncthreads();  // the tile holds this layer's input; every wave is done with the stages
         CH_STORE(E, 0);
         __syncthreads();
@@ -704,8 +714,16 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
             CH_STEP(O, E, 1, true, true);
             ++s;
         } while (s + 2 < steps);
+        CH_LDN(Ea0, 0, 0);  // the next layer's stage 0 into E, free since stage s - 1 went to LDS
+        CH_LDN(Ea1, 1, 0);
+        CH_LDN(Ea2, 2, 0);
+        CH_LDN(Ea3, 3, 0);
         CH_STEP(E, O, 0, false, true);
         ++s;
+        CH_LDN(Oa0, 0, 1);  // and its stage 1 into O, stored into LDS by the step before
+        CH_LDN(Oa1, 1, 1);
+        CH_LDN(Oa2, 2, 1);
+        CH_LDN(Oa3, 3, 1);
         CH_STEP(O, E, 1, false, false);
         __syncthreads();  // every wave has read its row fragments of this layer
 
@@ -727,14 +745,17 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
                     const int k = 16 * wm + 4 * mt + q;
                     *(h4 *)(act + b_row + nt * 32 * 512 + 16 * (k ^ n) + 8 * g) = v;
                 }
+        a_src = a_nx;
+        KB = KB_nx;
+    }
 #undef CH_LDA
+#undef CH_LDN
 #undef CH_LOAD
 #undef CH_STORE
 #undef CH_FRAGS
 #undef CH_ROW
 #undef CH_MFMAS16
 #undef CH_STEP
-    }
     __syncthreads();
 
     // The last layer's outputs: 32 chunks of 16 bytes per row, rows within the batch.
