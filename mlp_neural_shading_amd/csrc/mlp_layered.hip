@@ -633,8 +633,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
         *(uint4 *)(d + 3 * 4096) = P##a3;                                                                      \
     } while (0)
 // K block kbg of the layer (16 features): weight fragments from stage buffer buf (its block kbg % 2),
-// row fragments from the activation tile; read together and waited for (see BIG_FRAGS).
-#define CH_FRAGS(A0, A1, A2, A3, B0, B1, B2, B3, buf, kbg)                                                     \
+// row fragments from the activation tile, requested together (the waits fall where they are used).
+#define CH_READ(A0, A1, A2, A3, B0, B1, B2, B3, buf, kbg)                                                      \
     do {                                                                                                       \
         const uint8_t *la = ast[buf] + a_rd + ((kbg) & 1) * 1024;                                              \
         const uint8_t *lb = act + b_row + 16 * ((2 * (kbg) + g) ^ n);                                          \
@@ -646,7 +646,6 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
         B1 = *(const h8 *)(lb + 1 * 32 * 512);                                                                 \
         B2 = *(const h8 *)(lb + 2 * 32 * 512);                                                                 \
         B3 = *(const h8 *)(lb + 3 * 32 * 512);                                                                 \
-        asm volatile("" ::"v"(A0), "v"(A1), "v"(A2), "v"(A3), "v"(B0), "v"(B1), "v"(B2), "v"(B3));             \
     } while (0)
 #define CH_ROW(mt, A, B0, B1, B2, B3)                                                                          \
     do {                                                                                                       \
@@ -661,20 +660,6 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
         CH_ROW(1, A1, B0, B1, B2, B3);                                                                         \
         CH_ROW(2, A2, B0, B1, B2, B3);                                                                         \
         CH_ROW(3, A3, B0, B1, B2, B3);                                                                         \
-    } while (0)
-// Stage s as in the tile above (staging set P, stage buffer buf = s % 2).
-#define CH_STEP(P, Q, buf, LOAD, STORE)                                                                        \
-    do {                                                                                                       \
-        if (LOAD)                                                                                              \
-            CH_LOAD(P, s + 2);                                                                                 \
-        CH_FRAGS(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3, buf, 2 * s + 1);                                      \
-        CH_MFMAS16(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3);                                                    \
-        CH_MFMAS16(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3);                                                    \
-        if (STORE) {                                                                                           \
-            CH_STORE(Q, (buf) ^ 1);                                                                            \
-            __syncthreads();                                                                                   \
-            CH_FRAGS(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, (buf) ^ 1, 2 * s + 2);                            \
-        }                                                                                                      \
     } while (0)
     CH_LOAD(E, 0);
     CH_LOAD(O, 1);
@@ -706,25 +691,54 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
         __syncthreads();  // the tile holds this layer's input; every wave is done with the stages
         CH_STORE(E, 0);
         __syncthreads();
-        CH_FRAGS(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, 0, 0);
+// Stage s split around its barrier (as PP_STEP above): block 1's fragments are read and the next
+// stage's weights stored while block 0's MFMAs run, the next stage's block 0 after the barrier while
+// block 1's run; LOADN requests weights two stages ahead (in the last two steps, the next layer's
+// first two stages).  -1.6 % on 16 layers of 256 against the unsplit order.
+#define CH_SPLIT(P, Q, buf, LOADN, STORE)                                                                      \
+    do {                                                                                                       \
+        LOADN;                                                                                                 \
+        CH_READ(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3, buf, 2 * s + 1);                                       \
+        if (STORE)                                                                                             \
+            CH_STORE(Q, (buf) ^ 1);                                                                            \
+        CH_MFMAS16(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3);                                                    \
+        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                                     \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                 \
+        }                                                                                                      \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                                     \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                                                 \
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                                 \
+        }                                                                                                      \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                                       \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                                     \
+        if (STORE) {                                                                                           \
+            __syncthreads();                                                                                   \
+            CH_READ(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, (buf) ^ 1, 2 * s + 2);                             \
+        }                                                                                                      \
+        CH_MFMAS16(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3);                                                    \
+        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                                     \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                 \
+        }                                                                                                      \
+        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_)                                                       \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                                     \
+    } while (0)
+        CH_READ(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, 0, 0);
         int s = 0;
-        do {  // stages s and s + 1, both followed by two more
-            CH_STEP(E, O, 0, true, true);
+        do {
+            CH_SPLIT(E, O, 0, CH_LOAD(E, s + 2), true);
             ++s;
-            CH_STEP(O, E, 1, true, true);
+            CH_SPLIT(O, E, 1, CH_LOAD(O, s + 2), true);
             ++s;
         } while (s + 2 < steps);
-        CH_LDN(Ea0, 0, 0);  // the next layer's stage 0 into E, free since stage s - 1 went to LDS
-        CH_LDN(Ea1, 1, 0);
-        CH_LDN(Ea2, 2, 0);
-        CH_LDN(Ea3, 3, 0);
-        CH_STEP(E, O, 0, false, true);
+        CH_SPLIT(E, O, 0, (CH_LDN(Ea0, 0, 0), CH_LDN(Ea1, 1, 0), CH_LDN(Ea2, 2, 0), CH_LDN(Ea3, 3, 0)), true);
         ++s;
-        CH_LDN(Oa0, 0, 1);  // and its stage 1 into O, stored into LDS by the step before
-        CH_LDN(Oa1, 1, 1);
-        CH_LDN(Oa2, 2, 1);
-        CH_LDN(Oa3, 3, 1);
-        CH_STEP(O, E, 1, false, false);
+        CH_SPLIT(O, E, 1, (CH_LDN(Oa0, 0, 1), CH_LDN(Oa1, 1, 1), CH_LDN(Oa2, 2, 1), CH_LDN(Oa3, 3, 1)), false);
+#undef CH_SPLIT
         __syncthreads();  // every wave has read its row fragments of this layer
 
         // Epilogue into the tile: lane (g, n) of tile (mt, nt) holds outputs 32 mt + 8 q + 4 g + i of
@@ -752,10 +766,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #undef CH_LDN
 #undef CH_LOAD
 #undef CH_STORE
-#undef CH_FRAGS
 #undef CH_ROW
+#undef CH_READ
 #undef CH_MFMAS16
-#undef CH_STEP
     __syncthreads();
 
     // The last layer's outputs: 32 chunks of 16 bytes per row, rows within the batch.
