@@ -82,6 +82,7 @@ def trace(args) -> dict:
                 st = _stats(sel)
                 full = rows[at + pos]["Kernel_Name"]
                 name = full[:full.rindex("(")].split("::")[-1]  # drop the argument list and scopes
+                name = name[5:] if name.startswith("void ") else name  # and the return type
                 out["by_position"].append({"phase": ph, "position": pos, "kernel": name, **st})
                 print("| %d | %d | `%s` | %d | %.2f | %.2f | %.2f | %.2f |" % (ph, pos, name, st["n"], st["mean"], st["median"],
                                                                       st["min"], st["max"]))
