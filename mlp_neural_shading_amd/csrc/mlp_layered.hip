@@ -6,12 +6,15 @@
 //   Y[r][o] = act(RNE16(b[o] + sum_k W[o][k] * X[r][k]))   (FP16 x FP16 products, FP32 accumulation;
 //   act = the leaky ReLU max(v, v * half(0.01)) in FP16 for every layer but the last)
 // -- the same arithmetic as the fused path ("Profiling neural material inference", "Experiment
-// setup" and "Bad versus good activation"), with the activations between layers in device memory.
+// setup" and "Bad versus good activation"), with the activations between layers in device memory
+// (within a chain of 256-wide layers, in LDS).
 //
-// Two tilings (v_mfma_f32_32x32x16_f16, weights = A operand, rows = B operand, as in the fused
-// kernel): layers whose padded output width is a multiple of 256 and whose rows are whole 16-byte
-// chunks run on a 256 x 256 workgroup tile with both operands staged through LDS (described
-// below, before the kernel); every other layer on this 128 x 256 one:
+// Three forms (v_mfma_f32_32x32x16_f16, weights = A operand, rows = B operand, as in the fused
+// kernel): runs of consecutive layers with 256 padded outputs and K of 128..256 go through one
+// launch that keeps the row tile's activations in LDS (layer_chain, described before it); other
+// layers whose padded output width is a multiple of 256 and whose rows are whole 16-byte chunks run
+// on a 256 x 256 workgroup tile with both operands staged through LDS (layer_gemm_big); every other
+// layer on this 128 x 256 one:
 //   - a workgroup (4 waves) computes 128 outputs x 256 rows; each wave owns 64 rows (two 32-row
 //     sample tiles) and all 128 outputs (four output tiles), so every A fragment read from LDS feeds
 //     two MFMAs and every B fragment four;
