@@ -64,7 +64,7 @@ int g_act_mode = MLP_ACT_VECTOR;
 
 // The layer-by-layer path (mlp_layered.hip) stands in the registry's place for shapes no fused kernel
 // serves: widths above MLP_FUSED_MAX_WIDTH or more than MLP_FUSED_MAX_LAYERS layers.
-const KernelEntry kLayered = {"mlp_layered<256-wide chains | gemm 256x256 | 128x256, fused epilogue>", 0, {}, true, MLP_LAYOUT_PACKED,
+const KernelEntry kLayered = {"mlp_layered<256/128-wide chains | gemm 256x256 | 128x256, fused epilogue>", 0, {}, true, MLP_LAYOUT_PACKED,
                               MLP_ACT_VECTOR, 256, 64, true, nullptr, nullptr};
 bool is_layered(const KernelEntry *e) { return e == &kLayered; }
 
@@ -522,12 +522,14 @@ int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t 
         auto y_of = [&](int j) { return j == L - 1 ? (uint16_t *)out_ptr + r0 * w[L] : (uint16_t *)buf[j & 1]; };
         auto ldy_of = [&](int j) { return (int64_t)(j == L - 1 ? w[L] : ld_max); };
         for (int l = 0; l < L && err == hipSuccess;) {
-            // A chain [l, e): layers of 256 padded outputs and K 128..256, the first reading whole
-            // 16-byte rows of exactly its K columns, the last writing 16-byte rows of 256 outputs.
+            // A chain [l, e): layers of one chain width (256 or 128 padded outputs), the first reading
+            // whole 16-byte rows of exactly its K columns, the last writing 16-byte rows of a multiple
+            // of 8 outputs.
+            const int cw = mlpk::layered_chain_width(w[l], w[l + 1]);
             int e = l;
-            while (e < L && e - l < mlpk::kChainMaxLayers && mlpk::layered_chainable(w[e], w[e + 1]))
+            while (cw && e < L && e - l < mlpk::kChainMaxLayers && mlpk::layered_chain_width(w[e], w[e + 1]) == cw)
                 ++e;
-            while (e - l >= 2 && !(w[e] == mlpk::kChainWidth && ldy_of(e - 1) % 8 == 0 && ((uintptr_t)y_of(e - 1) & 15) == 0))
+            while (e - l >= 2 && !(w[e] % 8 == 0 && ldy_of(e - 1) % 8 == 0 && ((uintptr_t)y_of(e - 1) & 15) == 0))
                 --e;
             const bool whole_x = w[l] == mlpk::layered_kin(w[l]) && ldx_of(l) % 8 == 0 && ((uintptr_t)x_of(l) & 15) == 0;
             if (e - l >= 2 && whole_x) {
@@ -536,9 +538,11 @@ int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t 
                 c.ldx = ldx_of(l);
                 c.y = y_of(e - 1);
                 c.ldy = ldy_of(e - 1);
+                c.width = cw;
+                c.wout_last = w[e];
                 c.image = (const uint8_t *)g_net.image;
                 c.rows = rows;
-                c.row_tiles = (rows + mlpk::kChainWidth - 1) / mlpk::kChainWidth;
+                c.row_tiles = (rows + 255) / 256;
                 c.n = e - l;
                 c.act_last = e < L;
                 for (int j = l; j < e; ++j) {

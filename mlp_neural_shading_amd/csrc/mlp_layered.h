@@ -41,29 +41,36 @@ struct LayerArgs {
 
 hipError_t launch_layer(const LayerArgs &p, hipStream_t stream);
 
-// A run of consecutive layers whose padded output width is 256 and whose K is 128..256, in one launch:
-// each workgroup keeps its 256 rows' activations in LDS from the first layer's input to the last
-// layer's output, so only the chain's input and output pass through device memory.
+// A run of consecutive layers of one padded output width (256, or 128) in one launch: each workgroup
+// keeps its 256 rows' activations in LDS from the first layer's input to the last layer's output, so
+// only the chain's input and output pass through device memory.
 constexpr int kChainMaxLayers = 64;
-constexpr int kChainWidth = 256;
 struct ChainArgs {
     const uint16_t *x;  // [rows][ldx] FP16: the first layer's input, kin[0] columns, rows 16-byte aligned
     int64_t ldx;
-    uint16_t *y;        // [rows][ldy] FP16: the last layer's 256 outputs, rows 16-byte aligned (may be x)
+    uint16_t *y;        // [rows][ldy] FP16: the last layer's wout_last outputs, rows 16-byte aligned (may be x)
     int64_t ldy;
+    int width;          // the chain's padded width: 256 or 128
+    int wout_last;      // outputs stored from the last layer: a multiple of 8, at most width
     const uint8_t *image;  // the layered weight image
     int64_t rows;
     int64_t row_tiles;     // ceil(rows / 256)
     int n;                 // layers in the chain, 2 .. kChainMaxLayers
     int act_last;          // 1: leaky ReLU after the chain's last layer too
     uint64_t off[kChainMaxLayers];  // byte offset of each layer's A fragments in the image
-    int kin[kChainMaxLayers];       // each layer's padded K: 128, 192 or 256
+    int kin[kChainMaxLayers];       // each layer's padded K: 128..256 in a 256-wide chain, 64 or 128 in a 128-wide one
 };
 
-// Whether layer l (real widths win -> wout) can sit in a chain (its input then comes from LDS).
-inline bool layered_chainable(int win, int wout)
+// The chain width a layer (real widths win -> wout) can sit in, or 0: its padded output width, with a
+// padded K of at most that width (and at least 128 in a 256-wide chain).
+inline int layered_chain_width(int win, int wout)
 {
-    return layered_kout(wout) == kChainWidth && layered_kin(win) >= 128 && layered_kin(win) <= kChainWidth;
+    const int kout = layered_kout(wout), kin = layered_kin(win);
+    if (kout == 256 && kin >= 128 && kin <= 256)
+        return 256;
+    if (kout == 128 && kin <= 128)
+        return 128;
+    return 0;
 }
 
 hipError_t launch_chain(const ChainArgs &c, hipStream_t stream);

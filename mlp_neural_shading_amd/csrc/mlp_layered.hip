@@ -561,25 +561,32 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #undef BIG_OUT_STORES
 }
 
-
-
-
-// ---- a chain of 256-wide layers: the row tile's activations stay in LDS ---------------------------
+// ---- chains of layers: the row tile's activations stay in LDS ---------------------------------
 //
-// For consecutive layers with 256 padded outputs and K of 128..256 (every layer of a 256-wide net),
-// one workgroup (the 2 x 2 waves of the tile above, 256 accumulators each in AGPRs) takes 256 rows
-// through all the chain's layers.  Its activations live in a 128 KB LDS tile (row r's 16-byte chunk k,
-// features 8 k .. 8 k + 7, at r * 512 + 16 (k ^ (r % 32)): the 32 rows of a fragment read or an
-// epilogue write hit 32 different chunk slots), which the first layer's input rows are copied into
-// and the last layer's outputs are copied out of; only the weights stream in, through two 16 KB
-// stages per 32-deep K step, as in the tile above.  A layer's epilogue (nearest-even rounding, the
-// leaky ReLU) writes its outputs back into the tile, where the padded outputs (zero weights and bias)
-// are exact zeros for the next layer's padded K.  Device-memory traffic per chain: its input and its
-// output, instead of every layer's, which makes a 256-wide net bound by the MFMA pipe instead of HBM.
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void layer_chain(ChainArgs c)
+// For consecutive layers whose padded output width is CW (256, or 128 for narrow deep nets) and whose
+// K is at most CW, one workgroup of 2 x 2 waves takes 256 rows through all the chain's layers; each
+// wave computes CW / 2 outputs x 128 rows (CW / 64 x 4 MFMA tiles: 256 accumulators in AGPRs for
+// CW = 256, one workgroup per CU; 128 for CW = 128, two workgroups per CU).  The activations live in
+// an LDS tile of 256 rows x CW features (row r's 16-byte chunk k, features 8 k .. 8 k + 7, at
+// r * 2 CW + 16 (k ^ (r % (CW / 8))): the rows of a fragment read or an epilogue write hit distinct
+// chunk slots), which the first layer's input rows are copied into and the last layer's outputs are
+// copied out of; only the weights stream in, through two stages of CW x 32 K per step, as in the tile
+// above.  A layer's epilogue (nearest-even rounding, the leaky ReLU) writes its outputs back into the
+// tile, where the padded outputs (zero weights and bias) are exact zeros for the next layer's padded
+// K.  Device-memory traffic per chain: its input and its output, instead of every layer's, which
+// makes such nets bound by the MFMA pipe instead of HBM.
+template <int CW>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(CW == 256 ? 1 : 2, CW == 256 ? 1 : 2)))
+void layer_chain(ChainArgs c)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t act[BN * 512];
-    __shared__ __attribute__((aligned(16))) uint8_t ast[2][A_STAGE];
+    constexpr int MTC = CW / 64;        // output tiles per wave
+    constexpr int NA = CW / 64;         // 16-byte weight chunks per thread per stage
+    constexpr int ROWB = CW * 2;        // bytes per activation row
+    constexpr int NCH = CW / 8;         // 16-byte chunks per activation row
+    constexpr int SWZ = NCH - 1;
+    constexpr int A_ST = CW * BK * 2;   // weight stage bytes
+    __shared__ __attribute__((aligned(16))) uint8_t act[BN * ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t ast[2][A_ST];
 
     const int64_t rt = blockIdx.x;
     if (rt >= c.row_tiles)
@@ -597,23 +604,25 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
             const int r = i / kc, k = i - r * kc;
             const int64_t row = row0 + r < c.rows ? row0 + r : c.rows - 1;
             const uint4 v = *(const uint4 *)(c.x + row * c.ldx + 8 * k);
-            *(uint4 *)(act + r * 512 + 16 * (k ^ (r & 31))) = v;
+            *(uint4 *)(act + r * ROWB + 16 * (k ^ (r & SWZ))) = v;
         }
     }
 
     const h4 s4 = (h4)slope();
     // B fragment rows of this lane: tile nt's row wn * 128 + 32 nt + n, whose chunk k sits at
-    // row * 512 + 16 (k ^ n).
-    const int b_row = (wn * NTW * 32 + n) * 512;
-    const int a_rd = lane * 16 + wm * MTW * 2 * 1024;
+    // row * ROWB + 16 (k ^ (n % NCH)).
+    const int b_row = (wn * NTW * 32 + n) * ROWB;
+    const int b_swz = n & SWZ;
+    const int a_rd = lane * 16 + wm * MTC * 2 * 1024;
     uint4 Ea0, Ea1, Ea2, Ea3, Oa0, Oa1, Oa2, Oa3;
     h8 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3;
     h8 qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3;
-    f16x acc[MTW][NTW];
+    f16x acc[MTC][NTW];
 
     // Weight stages: a_src / KB describe the layer being computed; its first two stages are loaded
     // before it starts (for layer 0 here, for the others during the last two K steps of the layer
-    // before, into the staging registers those steps no longer use).
+    // before, into the staging registers those steps no longer use).  Thread chunk i of a stage is
+    // fragment f = wave + 4 i (output tile f / 2, K block f % 2).
     const uint8_t *a_src = c.image + c.off[0] + lane * 16;
     int KB = c.kin[0] / 16;
 #define CH_LDA(R, i, stage)                                                                                    \
@@ -624,31 +633,46 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
     do {                                                                                                       \
         CH_LDA(P##a0, 0, stage);                                                                               \
         CH_LDA(P##a1, 1, stage);                                                                               \
-        CH_LDA(P##a2, 2, stage);                                                                               \
-        CH_LDA(P##a3, 3, stage);                                                                               \
+        if constexpr (NA > 2) {                                                                                \
+            CH_LDA(P##a2, 2, stage);                                                                           \
+            CH_LDA(P##a3, 3, stage);                                                                           \
+        }                                                                                                      \
+    } while (0)
+#define CH_LOADN(P, stage)                                                                                     \
+    do {                                                                                                       \
+        CH_LDN(P##a0, 0, stage);                                                                               \
+        CH_LDN(P##a1, 1, stage);                                                                               \
+        if constexpr (NA > 2) {                                                                                \
+            CH_LDN(P##a2, 2, stage);                                                                           \
+            CH_LDN(P##a3, 3, stage);                                                                           \
+        }                                                                                                      \
     } while (0)
 #define CH_STORE(P, buf)                                                                                       \
     do {                                                                                                       \
         uint8_t *d = ast[buf] + wave * 1024 + lane * 16;                                                       \
         *(uint4 *)(d + 0 * 4096) = P##a0;                                                                      \
         *(uint4 *)(d + 1 * 4096) = P##a1;                                                                      \
-        *(uint4 *)(d + 2 * 4096) = P##a2;                                                                      \
-        *(uint4 *)(d + 3 * 4096) = P##a3;                                                                      \
+        if constexpr (NA > 2) {                                                                                \
+            *(uint4 *)(d + 2 * 4096) = P##a2;                                                                  \
+            *(uint4 *)(d + 3 * 4096) = P##a3;                                                                  \
+        }                                                                                                      \
     } while (0)
 // K block kbg of the layer (16 features): weight fragments from stage buffer buf (its block kbg % 2),
 // row fragments from the activation tile, requested together (the waits fall where they are used).
 #define CH_READ(A0, A1, A2, A3, B0, B1, B2, B3, buf, kbg)                                                      \
     do {                                                                                                       \
         const uint8_t *la = ast[buf] + a_rd + ((kbg) & 1) * 1024;                                              \
-        const uint8_t *lb = act + b_row + 16 * ((2 * (kbg) + g) ^ n);                                          \
+        const uint8_t *lb = act + b_row + 16 * ((2 * (kbg) + g) ^ b_swz);                                      \
         A0 = *(const h8 *)(la + 0 * 2048);                                                                     \
         A1 = *(const h8 *)(la + 1 * 2048);                                                                     \
-        A2 = *(const h8 *)(la + 2 * 2048);                                                                     \
-        A3 = *(const h8 *)(la + 3 * 2048);                                                                     \
-        B0 = *(const h8 *)(lb + 0 * 32 * 512);                                                                 \
-        B1 = *(const h8 *)(lb + 1 * 32 * 512);                                                                 \
-        B2 = *(const h8 *)(lb + 2 * 32 * 512);                                                                 \
-        B3 = *(const h8 *)(lb + 3 * 32 * 512);                                                                 \
+        if constexpr (MTC > 2) {                                                                               \
+            A2 = *(const h8 *)(la + 2 * 2048);                                                                 \
+            A3 = *(const h8 *)(la + 3 * 2048);                                                                 \
+        }                                                                                                      \
+        B0 = *(const h8 *)(lb + 0 * 32 * ROWB);                                                                \
+        B1 = *(const h8 *)(lb + 1 * 32 * ROWB);                                                                \
+        B2 = *(const h8 *)(lb + 2 * 32 * ROWB);                                                                \
+        B3 = *(const h8 *)(lb + 3 * 32 * ROWB);                                                                \
     } while (0)
 #define CH_ROW(mt, A, B0, B1, B2, B3)                                                                          \
     do {                                                                                                       \
@@ -657,27 +681,31 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
         acc[mt][2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B2, acc[mt][2], 0, 0, 0);                       \
         acc[mt][3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B3, acc[mt][3], 0, 0, 0);                       \
     } while (0)
-#define CH_MFMAS16(A0, A1, A2, A3, B0, B1, B2, B3)                                                             \
+#define CH_MFMAS(A0, A1, A2, A3, B0, B1, B2, B3)                                                               \
     do {                                                                                                       \
         CH_ROW(0, A0, B0, B1, B2, B3);                                                                         \
         CH_ROW(1, A1, B0, B1, B2, B3);                                                                         \
-        CH_ROW(2, A2, B0, B1, B2, B3);                                                                         \
-        CH_ROW(3, A3, B0, B1, B2, B3);                                                                         \
+        if constexpr (MTC > 2) {                                                                               \
+            CH_ROW(2, A2, B0, B1, B2, B3);                                                                     \
+            CH_ROW(3, A3, B0, B1, B2, B3);                                                                     \
+        }                                                                                                      \
     } while (0)
+    // per K block: MTC + 4 fragment reads and MTC x 4 MFMAs; per stage NA weight chunks per thread
+    constexpr int RD = MTC + 4, NM = MTC * 4;
     CH_LOAD(E, 0);
     CH_LOAD(O, 1);
 
     for (int l = 0; l < c.n; ++l) {
         const uint8_t *A = c.image + c.off[l];
-        const int steps = KB / 2;  // 4, 6 or 8
+        const int steps = KB / 2;  // 2 (CW = 128 only), 4, 6 or 8
         // the next layer's weights (the last layer reloads its own, unused: no branch)
         const int ln = l + 1 < c.n ? l + 1 : l;
         const uint8_t *a_nx = c.image + c.off[ln] + lane * 16;
         const int KB_nx = c.kin[ln] / 16;
-        const f4 *bias = (const f4 *)(A + (size_t)KB * 16 * 512);  // after the 8 x KB fragments
+        const f4 *bias = (const f4 *)(A + (size_t)(CW / 32) * KB * 1024);  // after the fragments
 #pragma unroll
-        for (int mt = 0; mt < MTW; ++mt) {
-            const f4 *bt = bias + (wm * MTW + mt) * 8 + g * 4;
+        for (int mt = 0; mt < MTC; ++mt) {
+            const f4 *bt = bias + (wm * MTC + mt) * 8 + g * 4;
             const f4 b0 = bt[0], b1 = bt[1], b2 = bt[2], b3 = bt[3];
             f16x b;
 #pragma unroll
@@ -704,52 +732,54 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
         CH_READ(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3, buf, 2 * s + 1);                                       \
         if (STORE)                                                                                             \
             CH_STORE(Q, (buf) ^ 1);                                                                            \
-        CH_MFMAS16(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3);                                                    \
-        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                                     \
+        CH_MFMAS(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3);                                                      \
+        _Pragma("unroll") for (int i_ = 0; i_ < RD; ++i_) {                                                    \
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                 \
         }                                                                                                      \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                                     \
+        _Pragma("unroll") for (int i_ = 0; i_ < NA; ++i_) {                                                    \
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                                                 \
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                                 \
         }                                                                                                      \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < NM - RD - NA; ++i_)                                            \
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
         __builtin_amdgcn_sched_barrier(0);                                                                     \
         if (STORE) {                                                                                           \
             __syncthreads();                                                                                   \
             CH_READ(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, (buf) ^ 1, 2 * s + 2);                             \
         }                                                                                                      \
-        CH_MFMAS16(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3);                                                    \
-        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                                     \
+        CH_MFMAS(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3);                                                      \
+        _Pragma("unroll") for (int i_ = 0; i_ < RD; ++i_) {                                                    \
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                 \
         }                                                                                                      \
-        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_)                                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < NM - RD; ++i_)                                                 \
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
         __builtin_amdgcn_sched_barrier(0);                                                                     \
     } while (0)
         CH_READ(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, 0, 0);
         int s = 0;
-        do {
-            CH_SPLIT(E, O, 0, CH_LOAD(E, s + 2), true);
-            ++s;
-            CH_SPLIT(O, E, 1, CH_LOAD(O, s + 2), true);
-            ++s;
-        } while (s + 2 < steps);
-        CH_SPLIT(E, O, 0, (CH_LDN(Ea0, 0, 0), CH_LDN(Ea1, 1, 0), CH_LDN(Ea2, 2, 0), CH_LDN(Ea3, 3, 0)), true);
+        if (CW == 256 || steps > 2) {  // K of 128..256 (the 256-wide chain always: no branch there)
+            do {
+                CH_SPLIT(E, O, 0, CH_LOAD(E, s + 2), true);
+                ++s;
+                CH_SPLIT(O, E, 1, CH_LOAD(O, s + 2), true);
+                ++s;
+            } while (s + 2 < steps);
+        }
+        CH_SPLIT(E, O, 0, CH_LOADN(E, 0), true);
         ++s;
-        CH_SPLIT(O, E, 1, (CH_LDN(Oa0, 0, 1), CH_LDN(Oa1, 1, 1), CH_LDN(Oa2, 2, 1), CH_LDN(Oa3, 3, 1)), false);
+        CH_SPLIT(O, E, 1, CH_LOADN(O, 1), false);
 #undef CH_SPLIT
         __syncthreads();  // every wave has read its row fragments of this layer
 
         // Epilogue into the tile: lane (g, n) of tile (mt, nt) holds outputs 32 mt + 8 q + 4 g + i of
         // row 32 nt + n (within the wave's quarter): features 8 k + 4 g .. + 3 of chunk
-        // k = 16 wm + 4 mt + q.
+        // k = (NCH / 2) wm + 4 mt + q.
         const bool act_l = l + 1 < c.n || c.act_last;
 #pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
+        for (int mt = 0; mt < MTC; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
@@ -759,8 +789,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
                     h4 v = __builtin_convertvector(part, h4);  // nearest even
                     if (act_l)
                         v = __builtin_elementwise_max(v, v * s4);
-                    const int k = 16 * wm + 4 * mt + q;
-                    *(h4 *)(act + b_row + nt * 32 * 512 + 16 * (k ^ n) + 8 * g) = v;
+                    const int k = (NCH / 2) * wm + 4 * mt + q;
+                    *(h4 *)(act + b_row + nt * 32 * ROWB + 16 * (k ^ b_swz) + 8 * g) = v;
                 }
         a_src = a_nx;
         KB = KB_nx;
@@ -768,18 +798,20 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #undef CH_LDA
 #undef CH_LDN
 #undef CH_LOAD
+#undef CH_LOADN
 #undef CH_STORE
 #undef CH_ROW
 #undef CH_READ
-#undef CH_MFMAS16
+#undef CH_MFMAS
     __syncthreads();
 
-    // The last layer's outputs: 32 chunks of 16 bytes per row, rows within the batch.
-    for (int i = tid; i < BN * 32; i += THREADS) {
-        const int r = i >> 5, k = i & 31;
-        if (row0 + r < c.rows)
-            *(uint4 *)(c.y + (row0 + r) * c.ldy + 8 * k) = *(const uint4 *)(act + r * 512 + 16 * (k ^ (r & 31)));
-    }
+    // The last layer's outputs: its first c.wout_last features (a multiple of 8) of each row within
+    // the batch, in 16-byte chunks; thread tid copies chunk tid % NCH of every (THREADS / NCH)-th row.
+    const int k = tid % NCH;
+    if (8 * k < c.wout_last)
+        for (int r = tid / NCH; r < BN; r += THREADS / NCH)
+            if (row0 + r < c.rows)
+                *(uint4 *)(c.y + (row0 + r) * c.ldy + 8 * k) = *(const uint4 *)(act + r * ROWB + 16 * (k ^ (r & SWZ)));
 }
 
 }  // namespace bigtile
@@ -815,7 +847,10 @@ hipError_t launch_layer(const LayerArgs &p, hipStream_t stream)
 
 hipError_t launch_chain(const ChainArgs &c, hipStream_t stream)
 {
-    hipLaunchKernelGGL(bigtile::layer_chain, dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
+    if (c.width == 256)
+        hipLaunchKernelGGL(bigtile::layer_chain<256>, dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
+    else
+        hipLaunchKernelGGL(bigtile::layer_chain<128>, dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
     return hipGetLastError();
 }
 

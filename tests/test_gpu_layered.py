@@ -176,15 +176,19 @@ def test_full_width_tiles_bit_exact(oracle_mod, rows):
     assert np.array_equal(run(Ws, bs, xs), oracle_mod.mlp_forward(Ws, bs, xs, threads=host_threads()))
 
 
-@pytest.mark.parametrize("widths", [(128, 256, 256, 200, 256, 256), (64, 256, 256, 256, 100), (256,) * 17])
+@pytest.mark.parametrize("widths", [(128, 256, 256, 200, 256, 256), (64, 256, 256, 256, 100), (256,) * 17,
+                                    (64,) * 17 + (16,), (128,) * 13 + (16,),
+                                    (96, 100, 128, 64, 120, 40, 64, 128, 72, 8)])
 @pytest.mark.parametrize("rows", [517, 131849])
 def test_chained_layers_bit_exact(oracle_mod, widths, rows):
-    """Consecutive layers with 256 padded outputs and K of 128..256 run as one chain, the row tile's
-    activations kept in LDS: a whole net ending in a chain (K of 128, a 200-wide layer whose padded
-    outputs must be exact zeros for the next K, no activation after the last layer), a chain between
-    single layers (its last layer activated), and 16 layers of 256.  Integer-exact nets against
-    float64 sums of small integers, and a signed permutation chain against the oracle, bit for bit,
-    over a ragged last tile and many tiles."""
+    """Consecutive layers of one padded output width (256 with K of 128..256, or 128 with K of 64 or
+    128) run as one chain, the row tile's activations kept in LDS: a whole net ending in a 256-wide
+    chain (K of 128, a 200-wide layer whose padded outputs must be exact zeros for the next K, no
+    activation after the last layer), a chain between single layers (its last layer activated), 16
+    layers of 256; narrow deep nets as 128-wide chains (17 layers of 64 then 16 outputs, K of 64 in two
+    stages; 13 layers of 128; two single layers, then a chain over padded widths 120, 40 and 72 ending
+    in 8 outputs).  Integer-exact nets against float64 sums of small integers, and a signed
+    permutation chain against the oracle, bit for bit, over a ragged last tile and many tiles."""
     rng = np.random.default_rng(rows + len(widths))
     L = len(widths) - 1
     W = [np.zeros((widths[l + 1], widths[l])) for l in range(L)]
