@@ -193,8 +193,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     MLPL_STEP(steps - 2, bc, bn, ra0, ra1, rb0, rb1, false);
     MLPL_MFMAS(steps - 1, bn);
 
-    // Epilogue: lane (g, n) holds, for row 64 wave + 32 j + n, outputs 32 mt + 8 q + 4 g + i.
-    const h4 s4 = (h4)slope();
+    // Epilogue: lane (g, n) holds, for row 64 wave + 32 j + n, outputs 32 mt + 8 q + 4 g + i.  Without
+    // the activation the slope is 1: max(v, v * 1) is v bit for bit, and no select per register.
+    const h4 s4 = p.act ? (h4)slope() : (h4)(_Float16)1.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int cbase = (ot * (kBM / 32) + i) * 32 + 4 * g;
@@ -209,8 +210,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 const int c = cbase + 8 * q;
                 const f4 part = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                 h4 v = __builtin_convertvector(part, h4);  // nearest even
-                if (p.act)
-                    v = __builtin_elementwise_max(v, v * s4);
+                v = __builtin_elementwise_max(v, v * s4);
                 if (p.vec_y && c + 4 <= p.wout) {
                     *(h4 *)(yr + c) = v;
                 } else {
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
     // 32 nt + n); only the stores check the batch and the output width, on a few registers, so the
     // 256 accumulators stream out of the AGPRs instead of being spilled around branches.
     __syncthreads();
-    const h4 s4 = (h4)slope();
+    const h4 s4 = p.act ? (h4)slope() : (h4)(_Float16)1.0f;  // slope 1: max(v, v * 1) is v
     uint8_t *ob = &lds[0][0] + wave * 16384;
     const bool vec16 = p.ldy % 8 == 0 && ((uintptr_t)p.y & 15) == 0;
     const int ldy2 = (int)p.ldy * 2;  // FULL only: at most 256 rows x 8 KB past the resource's base
@@ -496,8 +496,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
         _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                        \
             const f4 part = {acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]}; \
             h4 v = __builtin_convertvector(part, h4); /* nearest even */                                       \
-            if (p.act)                                                                                         \
-                v = __builtin_elementwise_max(v, v * s4);                                                      \
+            v = __builtin_elementwise_max(v, v * s4);                                                          \
             const int c = 8 * (mt) + 2 * q + g;                                                                \
             *(h4 *)(ob + rl * 256 + 8 * (c ^ (rl & 31))) = v;                                                  \
         }                                                                                                      \
@@ -777,7 +776,9 @@ void layer_chain(ChainArgs c)
         // Epilogue into the tile: lane (g, n) of tile (mt, nt) holds outputs 32 mt + 8 q + 4 g + i of
         // row 32 nt + n (within the wave's quarter): features 8 k + 4 g .. + 3 of chunk
         // k = (NCH / 2) wm + 4 mt + q.
-        const bool act_l = l + 1 < c.n || c.act_last;
+        // A layer without the activation (the chain's last, unless act_last) takes slope 1, for which
+        // max(v, v * 1) is v bit for bit: one uniform select per layer instead of one per register.
+        const h4 sl = l + 1 < c.n || c.act_last ? s4 : (h4)(_Float16)1.0f;
 #pragma unroll
         for (int mt = 0; mt < MTC; ++mt)
 #pragma unroll
@@ -787,8 +788,7 @@ void layer_chain(ChainArgs c)
                     const f4 part = {acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2],
                                      acc[mt][nt][4 * q + 3]};
                     h4 v = __builtin_convertvector(part, h4);  // nearest even
-                    if (act_l)
-                        v = __builtin_elementwise_max(v, v * s4);
+                    v = __builtin_elementwise_max(v, v * sl);
                     const int k = (NCH / 2) * wm + 4 * mt + q;
                     *(h4 *)(act + b_row + nt * 32 * ROWB + 16 * (k ^ b_swz) + 8 * g) = v;
                 }

@@ -50,6 +50,13 @@ def test_layered_workloads_are_named_apart():
     # both run layer by layer: every width padded to the layered tiles
     assert B.mlp_plan_widths(wide.widths) == [64] + [1024] * 7 + [128]
     assert B.mlp_plan_widths(deep.widths) == [256] * 17
+    # the deep narrow nets: every output width padded to 128 (64-wide layers keep K = 64)
+    narrow = workloads.get("layered64deep")
+    assert narrow.widths == (64,) * 17 + (16,) and narrow.batch == 1 << 20
+    assert B.mlp_plan_widths(narrow.widths) == [64] + [128] * 17
+    narrow128 = workloads.get("layered128deep")
+    assert narrow128.widths == (128,) * 13 + (16,) and narrow128.batch == 1 << 20
+    assert B.mlp_plan_widths(narrow128.widths) == [128] * 14
 
 
 def test_layered_workload_refuses_the_row_major_layout():

@@ -77,10 +77,12 @@ def test_full_size_sampled(oracle_mod, name, n_random, edge):
     log("   ", compare(_rows_bits(y, idx), ref, what=wl.name), "rows checked", idx.size)
 
 
-# The layer-by-layer networks at the sizes the benchmark times (one block of rows each, every layer a
-# separate GEMM launch): the first and last row tiles and seeded random rows against the oracle
-# (the 1024-wide net costs ~6.4 M multiply-adds per row on the host, the 256-wide one ~1 M).
-@pytest.mark.parametrize("name,n_random,edge", [("layered1024", 1024, 256), ("layered256", 4096, 1024)])
+# The layer-by-layer networks at the sizes the benchmark times (one block of rows each; a GEMM launch
+# per layer, or one launch per chain of layers): the first and last row tiles and seeded random rows
+# against the oracle (the 1024-wide net costs ~6.4 M multiply-adds per row on the host, the 256-wide
+# one ~1 M, the deep narrow ones 0.07 M and 0.2 M).
+@pytest.mark.parametrize("name,n_random,edge", [("layered1024", 1024, 256), ("layered256", 4096, 1024),
+                                                ("layered64deep", 65536, 4096), ("layered128deep", 16384, 4096)])
 def test_layered_workload_full_size_sampled(oracle_mod, name, n_random, edge):
     import torch
 
