@@ -178,7 +178,7 @@ def test_full_width_tiles_bit_exact(oracle_mod, rows):
 
 @pytest.mark.parametrize("widths", [(128, 256, 256, 200, 256, 256), (64, 256, 256, 256, 100), (256,) * 17,
                                     (64,) * 17 + (16,), (128,) * 13 + (16,),
-                                    (96, 100, 128, 64, 120, 40, 64, 128, 72, 8)])
+                                    (96, 100, 128, 64, 120, 40, 64, 128, 72, 8), (128, 128, 128, 72, 300, 16)])
 @pytest.mark.parametrize("rows", [517, 131849])
 def test_chained_layers_bit_exact(oracle_mod, widths, rows):
     """Consecutive layers of one padded output width (256 with K of 128..256, or 128 with K of 64 or
@@ -187,7 +187,8 @@ def test_chained_layers_bit_exact(oracle_mod, widths, rows):
     activation after the last layer), a chain between single layers (its last layer activated), 16
     layers of 256; narrow deep nets as 128-wide chains (17 layers of 64 then 16 outputs, K of 64 in two
     stages; 13 layers of 128; two single layers, then a chain over padded widths 120, 40 and 72 ending
-    in 8 outputs).  Integer-exact nets against float64 sums of small integers, and a signed
+    in 8 outputs; a chain that stores 72 of its 128 outputs for a single layer to read with K padded
+    to 128).  Integer-exact nets against float64 sums of small integers, and a signed
     permutation chain against the oracle, bit for bit, over a ragged last tile and many tiles."""
     rng = np.random.default_rng(rows + len(widths))
     L = len(widths) - 1
