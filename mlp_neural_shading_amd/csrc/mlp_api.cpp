@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -522,15 +523,19 @@ int infer_layered(int64_t batch, const void *in_ptr, void *out_ptr, hipStream_t 
         auto y_of = [&](int j) { return j == L - 1 ? (uint16_t *)out_ptr + r0 * w[L] : (uint16_t *)buf[j & 1]; };
         auto ldy_of = [&](int j) { return (int64_t)(j == L - 1 ? w[L] : ld_max); };
         for (int l = 0; l < L && err == hipSuccess;) {
-            // A chain [l, e): layers of one chain width (256 or 128 padded outputs), the first reading
-            // whole 16-byte rows of exactly its K columns, the last writing 16-byte rows of a multiple
-            // of 8 outputs.
-            const int cw = mlpk::layered_chain_width(w[l], w[l + 1]);
+            // A chain [l, e): layers that run at one chain width (all 256; or 128 and 64, at 64 when
+            // every layer is of class 64), the first reading whole 16-byte rows of exactly its K
+            // columns, the last writing 16-byte rows of a multiple of 8 outputs.
+            const int k0 = mlpk::layered_chain_class(w[l], w[l + 1]);
             int e = l;
-            while (cw && e < L && e - l < mlpk::kChainMaxLayers && mlpk::layered_chain_width(w[e], w[e + 1]) == cw)
+            while (k0 && e < L && e - l < mlpk::kChainMaxLayers &&
+                   mlpk::layered_chain_joins(k0, mlpk::layered_chain_class(w[e], w[e + 1])))
                 ++e;
             while (e - l >= 2 && !(w[e] % 8 == 0 && ldy_of(e - 1) % 8 == 0 && ((uintptr_t)y_of(e - 1) & 15) == 0))
                 --e;
+            int cw = 0;
+            for (int j = l; j < e; ++j)
+                cw = std::max(cw, mlpk::layered_chain_class(w[j], w[j + 1]));
             const bool whole_x = w[l] == mlpk::layered_kin(w[l]) && ldx_of(l) % 8 == 0 && ((uintptr_t)x_of(l) & 15) == 0;
             if (e - l >= 2 && whole_x) {
                 mlpk::ChainArgs c{};

@@ -41,16 +41,16 @@ struct LayerArgs {
 
 hipError_t launch_layer(const LayerArgs &p, hipStream_t stream);
 
-// A run of consecutive layers of one padded output width (256, or 128) in one launch: each workgroup
-// keeps its 256 rows' activations in LDS from the first layer's input to the last layer's output, so
-// only the chain's input and output pass through device memory.
+// A run of consecutive layers of one chain width (256, 128 or 64) in one launch: each workgroup keeps
+// its 256 rows' activations in LDS from the first layer's input to the last layer's output, so only
+// the chain's input and output pass through device memory.
 constexpr int kChainMaxLayers = 64;
 struct ChainArgs {
     const uint16_t *x;  // [rows][ldx] FP16: the first layer's input, kin[0] columns, rows 16-byte aligned
     int64_t ldx;
     uint16_t *y;        // [rows][ldy] FP16: the last layer's wout_last outputs, rows 16-byte aligned (may be x)
     int64_t ldy;
-    int width;          // the chain's padded width: 256 or 128
+    int width;          // the chain's width: 256, 128 or 64 (outputs computed per layer)
     int wout_last;      // outputs stored from the last layer: a multiple of 8, at most width
     const uint8_t *image;  // the layered weight image
     int64_t rows;
@@ -58,20 +58,28 @@ struct ChainArgs {
     int n;                 // layers in the chain, 2 .. kChainMaxLayers
     int act_last;          // 1: leaky ReLU after the chain's last layer too
     uint64_t off[kChainMaxLayers];  // byte offset of each layer's A fragments in the image
-    int kin[kChainMaxLayers];       // each layer's padded K: 128..256 in a 256-wide chain, 64 or 128 in a 128-wide one
+    int kin[kChainMaxLayers];       // each layer's padded K: 128..256 (width 256), 64 or 128 (128), 64 (64)
 };
 
-// The chain width a layer (real widths win -> wout) can sit in, or 0: its padded output width, with a
-// padded K of at most that width (and at least 128 in a 256-wide chain).
-inline int layered_chain_width(int win, int wout)
+// The narrowest chain width a layer (real widths win -> wout) can run in, or 0: 256 for 256 padded
+// outputs and a padded K of 128..256; 64 for at most 64 outputs and K of 64 (the image pads its
+// outputs to 128; the chain skips the zero half); 128 for 128 padded outputs and K of at most 128.
+// A chain runs at the widest class of its layers: a 64 layer also runs in a 128-wide chain (its
+// outputs 64..127 then computed as the exact zeros of the padded weights), never in a 256-wide one.
+inline int layered_chain_class(int win, int wout)
 {
     const int kout = layered_kout(wout), kin = layered_kin(win);
     if (kout == 256 && kin >= 128 && kin <= 256)
         return 256;
+    if (wout <= 64 && kin == 64)
+        return 64;
     if (kout == 128 && kin <= 128)
         return 128;
     return 0;
 }
+
+// Whether a layer of class k can join a chain that starts with a layer of class k0 (both non-zero).
+inline bool layered_chain_joins(int k0, int k) { return k0 == 256 ? k == 256 : k == 64 || k == 128; }
 
 hipError_t launch_chain(const ChainArgs &c, hipStream_t stream);
 

@@ -562,20 +562,23 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 
 // ---- chains of layers: the row tile's activations stay in LDS ---------------------------------
 //
-// For consecutive layers whose padded output width is CW (256, or 128 for narrow deep nets) and whose
-// K is at most CW, one workgroup of 2 x 2 waves takes 256 rows through all the chain's layers; each
-// wave computes CW / 2 outputs x 128 rows (CW / 64 x 4 MFMA tiles: 256 accumulators in AGPRs for
-// CW = 256, one workgroup per CU; 128 for CW = 128, two workgroups per CU).  The activations live in
-// an LDS tile of 256 rows x CW features (row r's 16-byte chunk k, features 8 k .. 8 k + 7, at
-// r * 2 CW + 16 (k ^ (r % (CW / 8))): the rows of a fragment read or an epilogue write hit distinct
-// chunk slots), which the first layer's input rows are copied into and the last layer's outputs are
+// For consecutive layers whose padded output width is CW (256; 128 or 64 for narrow deep nets) and
+// whose K is at most CW (64 for CW = 64), one workgroup of 2 x 2 waves takes 256 rows through all the
+// chain's layers; each wave computes CW / 2 outputs x 128 rows (CW / 64 x 4 MFMA tiles: 256
+// accumulators in AGPRs for CW = 256, one workgroup per CU; 128 for CW = 128, two workgroups per CU;
+// 64 for CW = 64, three).  The activations live in an LDS tile of 256 rows x CW features (row r's
+// 16-byte chunk k, features 8 k .. 8 k + 7, at r * 2 CW + 16 (k ^ sw(r)) with sw(r) = r % (CW / 8), or
+// (r / 2) % 8 for CW = 64: the 16 rows that one 256-byte LDS cycle of a fragment read serves hit 16
+// distinct slots of the 64 banks), which the first layer's input rows are copied into and the last
+// layer's outputs are
 // copied out of; only the weights stream in, through two stages of CW x 32 K per step, as in the tile
 // above.  A layer's epilogue (nearest-even rounding, the leaky ReLU) writes its outputs back into the
 // tile, where the padded outputs (zero weights and bias) are exact zeros for the next layer's padded
-// K.  Device-memory traffic per chain: its input and its output, instead of every layer's, which
+// K.  At CW = 64 the image's outputs 64..127 of each layer (padded to 128, all zero) are skipped.  Device-memory traffic per chain: its input and its output, instead of every layer's, which
 // makes such nets bound by the MFMA pipe instead of HBM.
 template <int CW>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(CW == 256 ? 1 : 2, CW == 256 ? 1 : 2)))
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(CW == 256 ? 1 : CW == 128 ? 2 : 3,
+                                                                          CW == 256 ? 1 : CW == 128 ? 2 : 3)))
 void layer_chain(ChainArgs c)
 {
     constexpr int MTC = CW / 64;        // output tiles per wave
@@ -583,6 +586,8 @@ void layer_chain(ChainArgs c)
     constexpr int ROWB = CW * 2;        // bytes per activation row
     constexpr int NCH = CW / 8;         // 16-byte chunks per activation row
     constexpr int SWZ = NCH - 1;
+    constexpr int SWS = CW < 128 ? 1 : 0;  // sw(r) = (r >> SWS) & SWZ
+    constexpr int KOUT = CW < 128 ? 128 : CW;  // the image's padded outputs per layer
     constexpr int A_ST = CW * BK * 2;   // weight stage bytes
     __shared__ __attribute__((aligned(16))) uint8_t act[BN * ROWB];
     __shared__ __attribute__((aligned(16))) uint8_t ast[2][A_ST];
@@ -603,15 +608,15 @@ void layer_chain(ChainArgs c)
             const int r = i / kc, k = i - r * kc;
             const int64_t row = row0 + r < c.rows ? row0 + r : c.rows - 1;
             const uint4 v = *(const uint4 *)(c.x + row * c.ldx + 8 * k);
-            *(uint4 *)(act + r * ROWB + 16 * (k ^ (r & SWZ))) = v;
+            *(uint4 *)(act + r * ROWB + 16 * (k ^ ((r >> SWS) & SWZ))) = v;
         }
     }
 
     const h4 s4 = (h4)slope();
     // B fragment rows of this lane: tile nt's row wn * 128 + 32 nt + n, whose chunk k sits at
-    // row * ROWB + 16 (k ^ (n % NCH)).
+    // row * ROWB + 16 (k ^ sw(n)) (sw of the row depends on n alone).
     const int b_row = (wn * NTW * 32 + n) * ROWB;
-    const int b_swz = n & SWZ;
+    const int b_swz = (n >> SWS) & SWZ;
     const int a_rd = lane * 16 + wm * MTC * 2 * 1024;
     uint4 Ea0, Ea1, Ea2, Ea3, Oa0, Oa1, Oa2, Oa3;
     h8 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3;
@@ -631,7 +636,8 @@ void layer_chain(ChainArgs c)
 #define CH_LOAD(P, stage)                                                                                      \
     do {                                                                                                       \
         CH_LDA(P##a0, 0, stage);                                                                               \
-        CH_LDA(P##a1, 1, stage);                                                                               \
+        if constexpr (NA > 1)                                                                                  \
+            CH_LDA(P##a1, 1, stage);                                                                           \
         if constexpr (NA > 2) {                                                                                \
             CH_LDA(P##a2, 2, stage);                                                                           \
             CH_LDA(P##a3, 3, stage);                                                                           \
@@ -640,7 +646,8 @@ void layer_chain(ChainArgs c)
 #define CH_LOADN(P, stage)                                                                                     \
     do {                                                                                                       \
         CH_LDN(P##a0, 0, stage);                                                                               \
-        CH_LDN(P##a1, 1, stage);                                                                               \
+        if constexpr (NA > 1)                                                                                  \
+            CH_LDN(P##a1, 1, stage);                                                                           \
         if constexpr (NA > 2) {                                                                                \
             CH_LDN(P##a2, 2, stage);                                                                           \
             CH_LDN(P##a3, 3, stage);                                                                           \
@@ -650,7 +657,8 @@ void layer_chain(ChainArgs c)
     do {                                                                                                       \
         uint8_t *d = ast[buf] + wave * 1024 + lane * 16;                                                       \
         *(uint4 *)(d + 0 * 4096) = P##a0;                                                                      \
-        *(uint4 *)(d + 1 * 4096) = P##a1;                                                                      \
+        if constexpr (NA > 1)                                                                                  \
+            *(uint4 *)(d + 1 * 4096) = P##a1;                                                                  \
         if constexpr (NA > 2) {                                                                                \
             *(uint4 *)(d + 2 * 4096) = P##a2;                                                                  \
             *(uint4 *)(d + 3 * 4096) = P##a3;                                                                  \
@@ -663,7 +671,8 @@ void layer_chain(ChainArgs c)
         const uint8_t *la = ast[buf] + a_rd + ((kbg) & 1) * 1024;                                              \
         const uint8_t *lb = act + b_row + 16 * ((2 * (kbg) + g) ^ b_swz);                                      \
         A0 = *(const h8 *)(la + 0 * 2048);                                                                     \
-        A1 = *(const h8 *)(la + 1 * 2048);                                                                     \
+        if constexpr (MTC > 1)                                                                                 \
+            A1 = *(const h8 *)(la + 1 * 2048);                                                                 \
         if constexpr (MTC > 2) {                                                                               \
             A2 = *(const h8 *)(la + 2 * 2048);                                                                 \
             A3 = *(const h8 *)(la + 3 * 2048);                                                                 \
@@ -683,7 +692,8 @@ void layer_chain(ChainArgs c)
 #define CH_MFMAS(A0, A1, A2, A3, B0, B1, B2, B3)                                                               \
     do {                                                                                                       \
         CH_ROW(0, A0, B0, B1, B2, B3);                                                                         \
-        CH_ROW(1, A1, B0, B1, B2, B3);                                                                         \
+        if constexpr (MTC > 1)                                                                                 \
+            CH_ROW(1, A1, B0, B1, B2, B3);                                                                     \
         if constexpr (MTC > 2) {                                                                               \
             CH_ROW(2, A2, B0, B1, B2, B3);                                                                     \
             CH_ROW(3, A3, B0, B1, B2, B3);                                                                     \
@@ -696,12 +706,12 @@ void layer_chain(ChainArgs c)
 
     for (int l = 0; l < c.n; ++l) {
         const uint8_t *A = c.image + c.off[l];
-        const int steps = KB / 2;  // 2 (CW = 128 only), 4, 6 or 8
+        const int steps = KB / 2;  // 2 (CW = 128 or 64), 4, 6 or 8
         // the next layer's weights (the last layer reloads its own, unused: no branch)
         const int ln = l + 1 < c.n ? l + 1 : l;
         const uint8_t *a_nx = c.image + c.off[ln] + lane * 16;
         const int KB_nx = c.kin[ln] / 16;
-        const f4 *bias = (const f4 *)(A + (size_t)(CW / 32) * KB * 1024);  // after the fragments
+        const f4 *bias = (const f4 *)(A + (size_t)(KOUT / 32) * KB * 1024);  // after the fragments
 #pragma unroll
         for (int mt = 0; mt < MTC; ++mt) {
             const f4 *bt = bias + (wm * MTC + mt) * 8 + g * 4;
@@ -732,34 +742,38 @@ void layer_chain(ChainArgs c)
         if (STORE)                                                                                             \
             CH_STORE(Q, (buf) ^ 1);                                                                            \
         CH_MFMAS(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3);                                                      \
-        _Pragma("unroll") for (int i_ = 0; i_ < RD; ++i_) {                                                    \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                 \
+        if constexpr (CW >= 128) {                                                                             \
+            _Pragma("unroll") for (int i_ = 0; i_ < RD; ++i_) {                                                \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
+            }                                                                                                  \
+            _Pragma("unroll") for (int i_ = 0; i_ < NA; ++i_) {                                                \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                                             \
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                             \
+            }                                                                                                  \
+            _Pragma("unroll") for (int i_ = 0; i_ < NM - RD - NA; ++i_)                                        \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
         }                                                                                                      \
-        _Pragma("unroll") for (int i_ = 0; i_ < NA; ++i_) {                                                    \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                                                 \
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                                 \
-        }                                                                                                      \
-        _Pragma("unroll") for (int i_ = 0; i_ < NM - RD - NA; ++i_)                                            \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
         __builtin_amdgcn_sched_barrier(0);                                                                     \
         if (STORE) {                                                                                           \
             __syncthreads();                                                                                   \
             CH_READ(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, (buf) ^ 1, 2 * s + 2);                             \
         }                                                                                                      \
         CH_MFMAS(qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3);                                                      \
-        _Pragma("unroll") for (int i_ = 0; i_ < RD; ++i_) {                                                    \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                 \
+        if constexpr (CW >= 128) {                                                                             \
+            _Pragma("unroll") for (int i_ = 0; i_ < RD; ++i_) {                                                \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
+            }                                                                                                  \
+            _Pragma("unroll") for (int i_ = 0; i_ < NM - RD; ++i_)                                             \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
         }                                                                                                      \
-        _Pragma("unroll") for (int i_ = 0; i_ < NM - RD; ++i_)                                                 \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                 \
         __builtin_amdgcn_sched_barrier(0);                                                                     \
     } while (0)
         CH_READ(pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3, 0, 0);
         int s = 0;
-        if (CW == 256 || steps > 2) {  // K of 128..256 (the 256-wide chain always: no branch there)
+        if (CW == 256 || (CW == 128 && steps > 2)) {  // K of 128..256 (the 256-wide chain always: no branch there)
             do {
                 CH_SPLIT(E, O, 0, CH_LOAD(E, s + 2), true);
                 ++s;
@@ -811,7 +825,7 @@ void layer_chain(ChainArgs c)
     if (8 * k < c.wout_last)
         for (int r = tid / NCH; r < BN; r += THREADS / NCH)
             if (row0 + r < c.rows)
-                *(uint4 *)(c.y + (row0 + r) * c.ldy + 8 * k) = *(const uint4 *)(act + r * ROWB + 16 * (k ^ (r & SWZ)));
+                *(uint4 *)(c.y + (row0 + r) * c.ldy + 8 * k) = *(const uint4 *)(act + r * ROWB + 16 * (k ^ ((r >> SWS) & SWZ)));
 }
 
 }  // namespace bigtile
@@ -849,8 +863,12 @@ hipError_t launch_chain(const ChainArgs &c, hipStream_t stream)
 {
     if (c.width == 256)
         hipLaunchKernelGGL(bigtile::layer_chain<256>, dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
-    else
+    else if (c.width == 128)
         hipLaunchKernelGGL(bigtile::layer_chain<128>, dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
+    else if (c.width == 64)
+        hipLaunchKernelGGL(bigtile::layer_chain<64>, dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
