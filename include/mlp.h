@@ -61,8 +61,9 @@ enum {
 #define MLP_MAX_WIDTH 4096 /* ... of widths up to 4096 (see MLP_FUSED_*)                         */
 /* Networks within these limits run as one fused kernel (weights in LDS, activations in registers);
  * wider or deeper ones run layer by layer (one MFMA GEMM with the fused epilogue per layer, the
- * activations between layers in device memory; a run of layers of one padded width, 64, 128 or 256, as
- * one launch with the activations kept in LDS), packed layout and vector activation only. */
+ * activations between layers in device memory; a run of layers of equal width class, at most 64,
+ * at most 128 or 256 padded outputs, as one launch with the activations kept in LDS), packed layout
+ * and vector activation only. */
 #define MLP_FUSED_MAX_LAYERS 8
 #define MLP_FUSED_MAX_WIDTH 128
 
