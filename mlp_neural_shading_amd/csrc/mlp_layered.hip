@@ -566,7 +566,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 // whose K is at most CW (64 for CW = 64), one workgroup of 2 x 2 waves takes 256 rows through all the
 // chain's layers; each wave computes CW / 2 outputs x 128 rows (CW / 64 x 4 MFMA tiles: 256
 // accumulators in AGPRs for CW = 256, one workgroup per CU; 128 for CW = 128, two workgroups per CU;
-// 64 for CW = 64, three).  The activations live in an LDS tile of 256 rows x CW features (row r's
+// 64 for CW = 64, up to four).  The activations live in an LDS tile of 256 rows x CW features (row r's
 // 16-byte chunk k, features 8 k .. 8 k + 7, at r * 2 CW + 16 (k ^ sw(r)) with sw(r) = r % (CW / 8), or
 // (r / 2) % 8 for CW = 64: the 16 rows that one 256-byte LDS cycle of a fragment read serves hit 16
 // distinct slots of the 64 banks), which the first layer's input rows are copied into and the last
@@ -577,8 +577,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 // K.  At CW = 64 the image's outputs 64..127 of each layer (padded to 128, all zero) are skipped.  Device-memory traffic per chain: its input and its output, instead of every layer's, which
 // makes such nets bound by the MFMA pipe instead of HBM.
 template <int CW>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(CW == 256 ? 1 : CW == 128 ? 2 : 3,
-                                                                          CW == 256 ? 1 : CW == 128 ? 2 : 3)))
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(CW == 256 ? 1 : CW == 128 ? 2 : 4,
+                                                                          CW == 256 ? 1 : CW == 128 ? 2 : 4)))
 void layer_chain(ChainArgs c)
 {
     constexpr int MTC = CW / 64;        // output tiles per wave
