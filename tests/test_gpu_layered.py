@@ -211,6 +211,20 @@ def test_chained_layers_bit_exact(oracle_mod, widths, rows):
     assert np.array_equal(run(Ws, bs, xs), oracle_mod.mlp_forward(Ws, bs, xs, threads=host_threads()))
 
 
+@pytest.mark.parametrize("widths", [(60,) + (64,) * 9 + (12,), (120,) + (128,) * 9 + (60,), (250,) + (256,) * 4 + (100,)])
+@pytest.mark.parametrize("rows", [1029, 70001])
+def test_chains_between_unaligned_rows(oracle_mod, widths, rows):
+    """Chains read and write whole 16-byte rows of exactly their K columns: an input width below its
+    padding to 64 (rows of 120, 240 or 500 bytes) puts the first layer on a single GEMM launch, an
+    output width that is not a multiple of 8 the last, and the layers between stay one chain (64, 128
+    and 256 wide).  A signed permutation chain against the oracle, bit for bit."""
+    rng = np.random.default_rng(rows + widths[0])
+    Ws, bs = _signed_chain(widths, rng)
+    x = _x(rows, widths[0], rows + 5)
+    log("chain between unaligned rows", widths[:3], "layers", len(widths) - 1, "rows", rows)
+    assert np.array_equal(run(Ws, bs, x), oracle_mod.mlp_forward(Ws, bs, x, threads=host_threads()))
+
+
 def test_large_tile_random_net(oracle_mod):
     widths = (64, 1024, 1024, 1000, 16)
     Ws, bs = workloads.init_weights(widths, seed=21)
