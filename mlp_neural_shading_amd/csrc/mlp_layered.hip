@@ -563,26 +563,34 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 // ---- chains of layers: the row tile's activations stay in LDS ---------------------------------
 //
 // For consecutive layers whose padded output width is CW (256; 128 or 64 for narrow deep nets) and
-// whose K is at most CW (64 for CW = 64), one workgroup of 2 x 2 waves takes 256 rows through all the
-// chain's layers; each wave computes CW / 2 outputs x 128 rows (CW / 64 x 4 MFMA tiles: 256
-// accumulators in AGPRs for CW = 256, one workgroup per CU; 128 for CW = 128, two workgroups per CU;
-// 64 for CW = 64, up to four).  The activations live in an LDS tile of 256 rows x CW features (row r's
-// 16-byte chunk k, features 8 k .. 8 k + 7, at r * 2 CW + 16 (k ^ sw(r)) with sw(r) = r % (CW / 8), or
-// (r / 2) % 8 for CW = 64: the 16 rows that one 256-byte LDS cycle of a fragment read serves hit 16
+// whose K is at most CW (64 for CW = 64), one workgroup of NW waves takes 256 rows through all the
+// chain's layers; wave w computes CW / 2 outputs (half w % 2) x 512 / NW rows (group w / 2), as
+// CW / 64 x 16 / NW MFMA tiles.  CW = 256 runs eight waves of 128 outputs x 64 rows (128 accumulators,
+// two waves per SIMD in the one workgroup per CU that its 160 KB of LDS allow: 9 % faster than four
+// waves of 256 accumulators, one per SIMD, whose barrier and epilogue waits no other wave covered);
+// CW = 128 four waves of 64 x 128 (128 accumulators, two workgroups per CU); CW = 64 four of 32 x 128
+// (64, up to four workgroups).  The activations live in an LDS tile of 256 rows x CW features (row
+// r's 16-byte chunk k, features 8 k .. 8 k + 7, at r * 2 CW + 16 (k ^ sw(r)) with sw(r) = r % (CW / 8),
+// or (r / 2) % 8 for CW = 64: the 16 rows that one 256-byte LDS cycle of a fragment read serves hit 16
 // distinct slots of the 64 banks), which the first layer's input rows are copied into and the last
-// layer's outputs are
-// copied out of; only the weights stream in, through two stages of CW x 32 K per step, as in the tile
-// above.  A layer's epilogue (nearest-even rounding, the leaky ReLU) writes its outputs back into the
-// tile, where the padded outputs (zero weights and bias) are exact zeros for the next layer's padded
-// K.  At CW = 64 the image's outputs 64..127 of each layer (padded to 128, all zero) are skipped.  Device-memory traffic per chain: its input and its output, instead of every layer's, which
-// makes such nets bound by the MFMA pipe instead of HBM.
-template <int CW>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(CW == 256 ? 1 : CW == 128 ? 2 : 4,
-                                                                          CW == 256 ? 1 : CW == 128 ? 2 : 4)))
+// layer's outputs are copied out of; only the weights stream in, through two stages of CW x 32 K per
+// step, as in the tile above.  A layer's epilogue (nearest-even rounding, the leaky ReLU) writes its
+// outputs back into the tile, where the padded outputs (zero weights and bias) are exact zeros for
+// the next layer's padded K.  At CW = 64 the image's outputs 64..127 of each layer (padded to 128, all
+// zero) are skipped.  Device-memory traffic per chain: its input and its output, instead of every
+// layer's, which makes such nets bound by the MFMA pipe instead of HBM.
+constexpr int chain_waves_per_simd(int cw, int nw) { return cw == 64 ? 4 : cw == 128 ? 2 : nw / 4; }
+
+template <int CW, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(chain_waves_per_simd(CW, NW),
+                                                                          chain_waves_per_simd(CW, NW))))
 void layer_chain(ChainArgs c)
 {
+    constexpr int TH = 64 * NW;         // threads per workgroup
+    constexpr int NTC = 16 / NW;        // 32-row tiles per wave
     constexpr int MTC = CW / 64;        // output tiles per wave
-    constexpr int NA = CW / 64;         // 16-byte weight chunks per thread per stage
+    constexpr int NA = CW * 4 / TH;     // 16-byte weight chunks per thread per stage
+    static_assert((NW == 4 || NW == 8) && NA >= 1 && NA <= 4, "a stage is 1 to 4 chunks per thread");
     constexpr int ROWB = CW * 2;        // bytes per activation row
     constexpr int NCH = CW / 8;         // 16-byte chunks per activation row
     constexpr int SWZ = NCH - 1;
@@ -604,7 +612,7 @@ void layer_chain(ChainArgs c)
     // row; their outputs are never stored).
     {
         const int kc = c.kin[0] / 8;
-        for (int i = tid; i < BN * kc; i += THREADS) {
+        for (int i = tid; i < BN * kc; i += TH) {
             const int r = i / kc, k = i - r * kc;
             const int64_t row = row0 + r < c.rows ? row0 + r : c.rows - 1;
             const uint4 v = *(const uint4 *)(c.x + row * c.ldx + 8 * k);
@@ -613,26 +621,26 @@ void layer_chain(ChainArgs c)
     }
 
     const h4 s4 = (h4)slope();
-    // B fragment rows of this lane: tile nt's row wn * 128 + 32 nt + n, whose chunk k sits at
+    // B fragment rows of this lane: tile nt's row wn * 32 NTC + 32 nt + n, whose chunk k sits at
     // row * ROWB + 16 (k ^ sw(n)) (sw of the row depends on n alone).
-    const int b_row = (wn * NTW * 32 + n) * ROWB;
+    const int b_row = (wn * NTC * 32 + n) * ROWB;
     const int b_swz = (n >> SWS) & SWZ;
     const int a_rd = lane * 16 + wm * MTC * 2 * 1024;
     uint4 Ea0, Ea1, Ea2, Ea3, Oa0, Oa1, Oa2, Oa3;
     h8 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3;
     h8 qa0, qa1, qa2, qa3, qb0, qb1, qb2, qb3;
-    f16x acc[MTC][NTW];
+    f16x acc[MTC][NTC];
 
     // Weight stages: a_src / KB describe the layer being computed; its first two stages are loaded
     // before it starts (for layer 0 here, for the others during the last two K steps of the layer
     // before, into the staging registers those steps no longer use).  Thread chunk i of a stage is
-    // fragment f = wave + 4 i (output tile f / 2, K block f % 2).
+    // fragment f = wave + NW i (output tile f / 2, K block f % 2).
     const uint8_t *a_src = c.image + c.off[0] + lane * 16;
     int KB = c.kin[0] / 16;
 #define CH_LDA(R, i, stage)                                                                                    \
-    R = *(const uint4 *)(a_src + ((size_t)((wave + 4 * (i)) >> 1) * KB + 2 * (stage) + ((wave + 4 * (i)) & 1)) * 1024)
+    R = *(const uint4 *)(a_src + ((size_t)((wave + NW * (i)) >> 1) * KB + 2 * (stage) + ((wave + NW * (i)) & 1)) * 1024)
 #define CH_LDN(R, i, stage)                                                                                    \
-    R = *(const uint4 *)(a_nx + ((size_t)((wave + 4 * (i)) >> 1) * KB_nx + 2 * (stage) + ((wave + 4 * (i)) & 1)) * 1024)
+    R = *(const uint4 *)(a_nx + ((size_t)((wave + NW * (i)) >> 1) * KB_nx + 2 * (stage) + ((wave + NW * (i)) & 1)) * 1024)
 #define CH_LOAD(P, stage)                                                                                      \
     do {                                                                                                       \
         CH_LDA(P##a0, 0, stage);                                                                               \
@@ -656,12 +664,12 @@ void layer_chain(ChainArgs c)
 #define CH_STORE(P, buf)                                                                                       \
     do {                                                                                                       \
         uint8_t *d = ast[buf] + wave * 1024 + lane * 16;                                                       \
-        *(uint4 *)(d + 0 * 4096) = P##a0;                                                                      \
+        *(uint4 *)(d + 0 * NW * 1024) = P##a0;                                                                 \
         if constexpr (NA > 1)                                                                                  \
-            *(uint4 *)(d + 1 * 4096) = P##a1;                                                                  \
+            *(uint4 *)(d + 1 * NW * 1024) = P##a1;                                                             \
         if constexpr (NA > 2) {                                                                                \
-            *(uint4 *)(d + 2 * 4096) = P##a2;                                                                  \
-            *(uint4 *)(d + 3 * 4096) = P##a3;                                                                  \
+            *(uint4 *)(d + 2 * NW * 1024) = P##a2;                                                             \
+            *(uint4 *)(d + 3 * NW * 1024) = P##a3;                                                             \
         }                                                                                                      \
     } while (0)
 // K block kbg of the layer (16 features): weight fragments from stage buffer buf (its block kbg % 2),
@@ -679,15 +687,19 @@ void layer_chain(ChainArgs c)
         }                                                                                                      \
         B0 = *(const h8 *)(lb + 0 * 32 * ROWB);                                                                \
         B1 = *(const h8 *)(lb + 1 * 32 * ROWB);                                                                \
-        B2 = *(const h8 *)(lb + 2 * 32 * ROWB);                                                                \
-        B3 = *(const h8 *)(lb + 3 * 32 * ROWB);                                                                \
+        if constexpr (NTC > 2) {                                                                               \
+            B2 = *(const h8 *)(lb + 2 * 32 * ROWB);                                                            \
+            B3 = *(const h8 *)(lb + 3 * 32 * ROWB);                                                            \
+        }                                                                                                      \
     } while (0)
 #define CH_ROW(mt, A, B0, B1, B2, B3)                                                                          \
     do {                                                                                                       \
         acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B0, acc[mt][0], 0, 0, 0);                       \
         acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B1, acc[mt][1], 0, 0, 0);                       \
-        acc[mt][2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B2, acc[mt][2], 0, 0, 0);                       \
-        acc[mt][3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B3, acc[mt][3], 0, 0, 0);                       \
+        if constexpr (NTC > 2) {                                                                               \
+            acc[mt][2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B2, acc[mt][2], 0, 0, 0);                   \
+            acc[mt][3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B3, acc[mt][3], 0, 0, 0);                   \
+        }                                                                                                      \
     } while (0)
 #define CH_MFMAS(A0, A1, A2, A3, B0, B1, B2, B3)                                                               \
     do {                                                                                                       \
@@ -699,8 +711,8 @@ void layer_chain(ChainArgs c)
             CH_ROW(3, A3, B0, B1, B2, B3);                                                                     \
         }                                                                                                      \
     } while (0)
-    // per K block: MTC + 4 fragment reads and MTC x 4 MFMAs; per stage NA weight chunks per thread
-    constexpr int RD = MTC + 4, NM = MTC * 4;
+    // per K block: MTC + NTC fragment reads and MTC x NTC MFMAs; per stage NA weight chunks per thread
+    constexpr int RD = MTC + NTC, NM = MTC * NTC;
     CH_LOAD(E, 0);
     CH_LOAD(O, 1);
 
@@ -725,7 +737,7 @@ void layer_chain(ChainArgs c)
                 b[12 + j] = b3[j];
             }
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
+            for (int nt = 0; nt < NTC; ++nt)
                 acc[mt][nt] = b;
         }
         __syncthreads();  // the tile holds this layer's input; every wave is done with the stages
@@ -788,7 +800,7 @@ void layer_chain(ChainArgs c)
         __syncthreads();  // every wave has read its row fragments of this layer
 
         // Epilogue into the tile: lane (g, n) of tile (mt, nt) holds outputs 32 mt + 8 q + 4 g + i of
-        // row 32 nt + n (within the wave's quarter): features 8 k + 4 g .. + 3 of chunk
+        // row 32 nt + n (within the wave's row group): features 8 k + 4 g .. + 3 of chunk
         // k = (NCH / 2) wm + 4 mt + q.
         // A layer without the activation (the chain's last, unless act_last) takes slope 1, for which
         // max(v, v * 1) is v bit for bit: one uniform select per layer instead of one per register.
@@ -796,7 +808,7 @@ void layer_chain(ChainArgs c)
 #pragma unroll
         for (int mt = 0; mt < MTC; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
+            for (int nt = 0; nt < NTC; ++nt)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const f4 part = {acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1], acc[mt][nt][4 * q + 2],
@@ -820,10 +832,10 @@ void layer_chain(ChainArgs c)
     __syncthreads();
 
     // The last layer's outputs: its first c.wout_last features (a multiple of 8) of each row within
-    // the batch, in 16-byte chunks; thread tid copies chunk tid % NCH of every (THREADS / NCH)-th row.
+    // the batch, in 16-byte chunks; thread tid copies chunk tid % NCH of every (TH / NCH)-th row.
     const int k = tid % NCH;
     if (8 * k < c.wout_last)
-        for (int r = tid / NCH; r < BN; r += THREADS / NCH)
+        for (int r = tid / NCH; r < BN; r += TH / NCH)
             if (row0 + r < c.rows)
                 *(uint4 *)(c.y + (row0 + r) * c.ldy + 8 * k) = *(const uint4 *)(act + r * ROWB + 16 * (k ^ ((r >> SWS) & SWZ)));
 }
@@ -862,11 +874,11 @@ hipError_t launch_layer(const LayerArgs &p, hipStream_t stream)
 hipError_t launch_chain(const ChainArgs &c, hipStream_t stream)
 {
     if (c.width == 256)
-        hipLaunchKernelGGL(bigtile::layer_chain<256>, dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
+        hipLaunchKernelGGL((bigtile::layer_chain<256, 8>), dim3((unsigned)c.row_tiles), dim3(512), 0, stream, c);
     else if (c.width == 128)
-        hipLaunchKernelGGL(bigtile::layer_chain<128>, dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
+        hipLaunchKernelGGL((bigtile::layer_chain<128, 4>), dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
     else if (c.width == 64)
-        hipLaunchKernelGGL(bigtile::layer_chain<64>, dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
+        hipLaunchKernelGGL((bigtile::layer_chain<64, 4>), dim3((unsigned)c.row_tiles), dim3(bigtile::THREADS), 0, stream, c);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
