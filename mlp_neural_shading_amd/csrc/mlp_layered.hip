@@ -566,7 +566,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 // whose K is at most CW (64 for CW = 64), one workgroup of NW waves takes 256 rows through all the
 // chain's layers; wave w computes CW / 2 outputs (half w % 2) x 512 / NW rows (group w / 2), as
 // CW / 64 x 16 / NW MFMA tiles.  CW = 256 runs eight waves of 128 outputs x 64 rows (128 accumulators,
-// two waves per SIMD in the one workgroup per CU that its 160 KB of LDS allow: 9 % faster than four
+// two waves per SIMD in the one workgroup per CU that its 160 KB of LDS allow: 8-9 % faster than four
 // waves of 256 accumulators, one per SIMD, whose barrier and epilogue waits no other wave covered);
 // CW = 128 four waves of 64 x 128 (128 accumulators, two workgroups per CU); CW = 64 four of 32 x 128
 // (64, up to four workgroups).  The activations live in an LDS tile of 256 rows x CW features (row
