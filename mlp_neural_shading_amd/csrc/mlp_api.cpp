@@ -377,8 +377,8 @@ int mlp_testing_pack_device_on_host(int n_layers, const int32_t *widths, const u
         return fail(MLP_ERR_INVALID_ARGUMENT, "host_dst holds %zu bytes, the image has %zu", dst_bytes, need);
     std::vector<uint8_t> written(need, 0);
     bool clean = true;
-    for (int l0 = 0; l0 < n_layers; l0 += 8) {  // as mlp_pack_weights_device launches it
-        const int count = n_layers - l0 < 8 ? n_layers - l0 : 8;
+    for (int l0 = 0; l0 < n_layers; l0 += mlpk::kPackMaxLayers) {  // as mlp_pack_weights_device launches it
+        const int count = n_layers - l0 < mlpk::kPackMaxLayers ? n_layers - l0 : mlpk::kPackMaxLayers;
         mlpk::PackArgs args{};
         if (is_layered(e))
             mlpk::fill_pack_args_layered(widths, l0, count, args);
@@ -408,17 +408,17 @@ int mlp_pack_weights_device(int n_layers, const int32_t *widths, const void *con
     for (int l = 0; l < n_layers; ++l)
         if (((uintptr_t)d_weights[l] | (uintptr_t)d_biases[l]) & 1)
             return fail(MLP_ERR_INVALID_ARGUMENT, "d_weights[%d] or d_biases[%d] is not 2-byte aligned", l, l);
-    // One launch (at most 8 layers) rewrites an image of unchanged size in place: hipFree would wait for
+    // One launch (at most 16 layers) rewrites an image of unchanged size in place: hipFree would wait for
     // the whole device, and a conversion recorded into the stream should not.  Deeper networks take
     // several launches and a new image, so a failed launch never leaves the current network half
     // rewritten.
     State next;
-    rc = new_state(n_layers, widths, layout, e, next, n_layers <= 8);
+    rc = new_state(n_layers, widths, layout, e, next, n_layers <= mlpk::kPackMaxLayers);
     if (rc != MLP_OK)
         return rc;
-    // The conversion kernel takes up to 8 layers per launch.
-    for (int l0 = 0; l0 < n_layers; l0 += 8) {
-        const int count = n_layers - l0 < 8 ? n_layers - l0 : 8;
+    // The conversion kernel takes up to kPackMaxLayers layers per launch (a fused network in one).
+    for (int l0 = 0; l0 < n_layers; l0 += mlpk::kPackMaxLayers) {
+        const int count = n_layers - l0 < mlpk::kPackMaxLayers ? n_layers - l0 : mlpk::kPackMaxLayers;
         mlpk::PackArgs args{};
         if (is_layered(e))
             mlpk::fill_pack_args_layered(widths, l0, count, args);

@@ -908,6 +908,16 @@ static const KernelEntry kEntries[] = {
     MLP_GENERIC64V3(64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=6>"),
     MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=7>"),
     MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=8>"),
+    // deeper narrow nets (all widths at most 64), vector I/O only: the image of 16 layers takes
+    // ~140 KB of LDS (one workgroup of two waves per SIMD per CU)
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=9>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=10>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=11>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=12>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=13>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=14>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=15>"),
+    MLP_GENERIC64V(64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64)("mlp_fused<generic64v,L=16>"),
     MLP_GENERIC64(64, 64)("mlp_fused<generic64,L=1>"),
     MLP_GENERIC64(64, 64, 64)("mlp_fused<generic64,L=2>"),
     MLP_GENERIC64(64, 64, 64, 64)("mlp_fused<generic64,L=3>"),

@@ -25,18 +25,21 @@ void pack_image(int n_layers, const int *widths, const int *kernel_widths, const
 // FP8: 32-byte lane slices of the A fragments), [first[l], mid[l]) the FP8 scale codes (empty for
 // the FP16 layouts), [mid[l], items[l]) the biases; a_off / s_off / b_off are the byte offsets of
 // the sections.
+constexpr int kPackMaxLayers = 16;  // layers one conversion launch takes: every fused network
 struct PackArgs {
-    const uint16_t *w[8];
-    const uint16_t *b[8];
-    int win[8], wout[8], mt[8], kb[8];
-    int narrow[8];  // 1: the narrow last-layer layout of mlp_layout.h (packed layout, one output tile)
-    uint32_t a_off[8], s_off[8], b_off[8], first[8], mid[8], items[8];
+    const uint16_t *w[kPackMaxLayers];
+    const uint16_t *b[kPackMaxLayers];
+    int win[kPackMaxLayers], wout[kPackMaxLayers], mt[kPackMaxLayers], kb[kPackMaxLayers];
+    int narrow[kPackMaxLayers];  // 1: the narrow last-layer layout of mlp_layout.h (packed layout, one output tile)
+    uint32_t a_off[kPackMaxLayers], s_off[kPackMaxLayers], b_off[kPackMaxLayers], first[kPackMaxLayers],
+        mid[kPackMaxLayers], items[kPackMaxLayers];
     int layout;
     int natural;  // 1: every layer in natural K order (the layered image), 0: the fused kernels' order
     uint8_t *dst;
 };
 
-// Fill everything but w, b and dst for the caller's widths and the kernel's widths kw.
+// Fill everything but w, b and dst for the caller's widths and the kernel's widths kw (a fused network:
+// n_layers <= kPackMaxLayers).
 void fill_pack_args(int n_layers, const int *widths, const int *kw, int layout, PackArgs &p);
 
 // The layered path's image (mlp_layered.h): bytes, and the host packer.  Layers are packed one after

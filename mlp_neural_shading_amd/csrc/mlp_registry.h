@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "mlp.h"
+
 namespace mlpk {
 
 enum Layout { kRowMajor = 0, kPacked = 1, kPackedFp8 = 2 };
@@ -23,7 +25,7 @@ struct LaunchArgs {
 struct KernelEntry {
     const char *name;
     int n_layers;
-    int widths[9];      // exact instance: the widths it serves; generic: all 64 or all 128 (any shape within)
+    int widths[MLP_FUSED_NARROW_MAX_LAYERS + 1];  // exact instance: the widths it serves; generic: all 64 or all 128 (any shape within)
     bool generic;
     int layout;
     int act;

@@ -149,7 +149,11 @@ def test_plan_widths():
     assert B.mlp_plan_widths([2, 2, 1]) == [64, 64, 64]  # generic kernel, zero-padded to 64
     assert B.mlp_plan_widths([2, 65, 1]) == [128, 128, 128]  # a width above 64: the 128-wide family
     assert B.mlp_plan_widths([100, 300, 129, 7]) == [128, 384, 256, 128]  # layer by layer
-    assert B.mlp_plan_widths([16] * 10) == [64] + [128] * 9
+    assert B.mlp_plan_widths([16] * 10) == [64] * 10  # 9 narrow layers: the deep generic fused kernel
+    assert B.mlp_plan_widths([16] * 17) == [64] * 17  # 16 narrow layers: still fused
+    assert B.mlp_plan_widths([16] * 18) == [64] + [128] * 17  # 17 layers: layer by layer
+    assert B.mlp_plan_widths([12] + [16] * 9) == [64] + [128] * 9  # input width not a multiple of 8
+    assert B.mlp_plan_widths([16] * 9 + [65]) == [64] + [128] * 9  # a width above 64
 
 
 # ---- an independent reading of the layer-by-layer image ------------------------------------------
@@ -182,7 +186,7 @@ def _unpack_layered(image, widths):
     return Ws, bs
 
 
-@pytest.mark.parametrize("widths", [(100, 300, 129, 7), (16,) * 10, (256, 32, 200)])
+@pytest.mark.parametrize("widths", [(100, 300, 129, 7), (16,) * 18, (256, 32, 200)])
 def test_layered_image_layout(widths):
     Ws, bs = workloads.init_weights(widths, seed=5)
     image = B.mlp_pack_host(Ws, bs, B.MLP_LAYOUT_PACKED)

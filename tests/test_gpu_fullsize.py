@@ -185,7 +185,8 @@ def test_boundary_errors_on_device():
     (9, 65, 3),                             # generic, 128-wide, element by element
     (24, 40, 16, 72, 8, 100, 12, 56, 8),    # generic, 128-wide, vector I/O
     (64, 256, 256, 16),                     # layer by layer
-    (48,) * 13,                             # layer by layer, unaligned K
+    (48,) * 18,                             # layer by layer, unaligned K (a 64-wide chain)
+    (48,) * 13,                             # generic, 64-wide, 12 layers
 ])
 def test_batch_prefix_invariance_every_family(widths):
     import torch

@@ -1,6 +1,7 @@
-"""GPU parity of the layer-by-layer path (networks wider than 128 or deeper than 8 layers: one MFMA
-GEMM with the fused bias / rounding / leaky-ReLU epilogue per layer, "Profiling neural material
-inference", "Experiment setup") against the CPU oracle, through the C ABI.
+"""GPU parity of the layer-by-layer path (networks wider than 128, or deeper than 8 layers, or than 16
+when every width is at most 64: one MFMA GEMM with the fused bias / rounding / leaky-ReLU epilogue per
+layer, "Profiling neural material inference", "Experiment setup") against the CPU oracle, through
+the C ABI.
 
 - order-free nets (every partial sum exact): bit for bit against the oracle and int64 products;
 - permutation chains (the leaky slope on negative values through every layer): bit for bit;
@@ -30,7 +31,7 @@ def _x(rows, w, seed):
 
 @pytest.mark.parametrize("widths,rows", [
     ((64, 256, 256, 16), 4133),               # wider than 128
-    ((48,) * 13, 3000),                        # 12 layers
+    ((48,) * 18, 3000),                        # 17 layers
     ((100, 300, 129, 7), 1000),                # odd widths: unaligned input and output rows
     ((1024, 1024, 8), 700),                    # K = 1024
     ((16, 4096, 4), 257),                      # the widest layer allowed

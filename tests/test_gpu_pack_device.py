@@ -16,7 +16,9 @@ pytestmark = pytest.mark.gpu
 
 CASES = [(name, layout) for name in workloads.WORKLOADS
          for layout in (B.MLP_LAYOUT_PACKED, B.MLP_LAYOUT_ROW_MAJOR, B.MLP_LAYOUT_PACKED_FP8)]
-GENERIC = [(5, 7, 3), (2, 2, 1), (128,) * 9, (1, 128, 1), (17, 33, 65, 100, 3)]
+GENERIC = [(5, 7, 3), (2, 2, 1), (128,) * 9, (1, 128, 1), (17, 33, 65, 100, 3),
+           (32, 48, 64, 40, 64, 64, 8, 64, 56, 64, 64, 24, 64, 64, 64, 64, 12),  # 16 layers, fused
+           (16,) * 21]  # 20 layers, layer by layer: two conversion launches
 
 
 def _device_weights(Ws, bs):
