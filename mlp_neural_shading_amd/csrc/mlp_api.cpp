@@ -64,7 +64,8 @@ State g_net;
 int g_act_mode = MLP_ACT_VECTOR;
 
 // The layer-by-layer path (mlp_layered.hip) stands in the registry's place for shapes no fused kernel
-// serves: widths above MLP_FUSED_MAX_WIDTH or more than MLP_FUSED_MAX_LAYERS layers.
+// serves: widths above MLP_FUSED_MAX_WIDTH, more than MLP_FUSED_MAX_LAYERS layers of widths above 64,
+// or more than MLP_FUSED_NARROW_MAX_LAYERS.
 const KernelEntry kLayered = {"mlp_layered<256/128/64-wide chains | gemm 256x256 | 128x256, fused epilogue>", 0, {}, true, MLP_LAYOUT_PACKED,
                               MLP_ACT_VECTOR, 256, 64, true, nullptr, nullptr};
 bool is_layered(const KernelEntry *e) { return e == &kLayered; }

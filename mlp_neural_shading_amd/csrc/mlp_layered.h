@@ -1,5 +1,6 @@
-// mlp_layered.h -- the layer-by-layer path for networks beyond the fused kernels (widths > 128 or
-// more than 8 layers): geometry of its weight image and the per-layer kernel launch.
+// mlp_layered.h -- the layer-by-layer path for networks beyond the fused kernels (widths > 128, or
+// more than 8 layers, or more than 16 when every width is at most 64): geometry of its weight image
+// and the per-layer kernel launch.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
