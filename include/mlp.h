@@ -61,14 +61,16 @@ enum {
 #define MLP_MAX_WIDTH 4096 /* ... of widths up to 4096 (see MLP_FUSED_*)                         */
 /* Networks within these limits run as one fused kernel (weights in LDS, activations in registers):
  * up to MLP_FUSED_MAX_LAYERS layers of widths up to MLP_FUSED_MAX_WIDTH, or up to
- * MLP_FUSED_NARROW_MAX_LAYERS layers whose widths are all at most 64 (the input width a multiple of
- * 8, the output width of 4).  Wider or deeper ones run layer by layer (one MFMA GEMM with the fused
- * epilogue per layer, the activations between layers in device memory; a run of layers of equal
- * width class, at most 64, at most 128 or 256 padded outputs, as one launch with the activations kept
- * in LDS), packed layout and vector activation only. */
+ * MLP_FUSED_DEEP_MAX_LAYERS layers with the input width a multiple of 8 and the output width of 4:
+ * always when every width is at most 64, and at widths up to 128 unless the layer-by-layer path
+ * runs the whole network as one chain (every layer padded to 128 outputs, the input width a multiple
+ * of 64, the output width of 8), which is faster there.  Wider or deeper ones run layer by layer (one
+ * MFMA GEMM with the fused epilogue per layer, the activations between layers in device memory; a
+ * run of layers of equal width class, at most 64, at most 128 or 256 padded outputs, as one launch
+ * with the activations kept in LDS), packed layout and vector activation only. */
 #define MLP_FUSED_MAX_LAYERS 8
 #define MLP_FUSED_MAX_WIDTH 128
-#define MLP_FUSED_NARROW_MAX_LAYERS 16
+#define MLP_FUSED_DEEP_MAX_LAYERS 16
 
 /* Size in bytes of the device image mlp_pack_weights would build for this shape and layout: the
  * size query that precedes the one-time conversion ("Row-major versus InferencingOptimal weights":
@@ -86,9 +88,9 @@ int mlp_packed_size(int n_layers, const int32_t *widths, int layout, size_t *out
  * layer width padded to its tile multiple, except that a last layer of at most 4 outputs on a
  * dedicated FP16 kernel is computed 4 wide): kernel_widths receives n_layers + 1 entries.  Shapes
  * without a dedicated kernel but within the fused limits run on a generic fused kernel whose widths
- * are all 64 (when every width is at most 64; up to MLP_FUSED_NARROW_MAX_LAYERS layers) or all
- * MLP_FUSED_MAX_WIDTH, zero-padded; wider or deeper shapes run layer by layer with the input width
- * padded to a multiple of 64 and every layer width to a multiple of 128.
+ * are all 64 (when every width is at most 64) or all MLP_FUSED_MAX_WIDTH, zero-padded; wider or
+ * deeper shapes run layer by layer with the input width padded to a multiple of 64 and every layer
+ * width to a multiple of 128.
  * Host only; no HIP call. */
 int mlp_plan_widths(int n_layers, const int32_t *widths, int layout, int32_t *kernel_widths);
 

@@ -31,7 +31,7 @@ MLP_MAX_LAYERS = 64
 MLP_MAX_WIDTH = 4096
 MLP_FUSED_MAX_LAYERS = 8
 MLP_FUSED_MAX_WIDTH = 128
-MLP_FUSED_NARROW_MAX_LAYERS = 16
+MLP_FUSED_DEEP_MAX_LAYERS = 16
 
 EXPORTED = (
     "mlp_packed_size", "mlp_plan_widths", "mlp_pack_host", "mlp_pack_weights", "mlp_pack_weights_device",

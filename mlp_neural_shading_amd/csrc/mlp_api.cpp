@@ -64,8 +64,8 @@ State g_net;
 int g_act_mode = MLP_ACT_VECTOR;
 
 // The layer-by-layer path (mlp_layered.hip) stands in the registry's place for shapes no fused kernel
-// serves: widths above MLP_FUSED_MAX_WIDTH, more than MLP_FUSED_MAX_LAYERS layers of widths above 64,
-// or more than MLP_FUSED_NARROW_MAX_LAYERS.
+// serves: widths above MLP_FUSED_MAX_WIDTH, more than MLP_FUSED_DEEP_MAX_LAYERS layers, or more than
+// MLP_FUSED_MAX_LAYERS without vector I/O or, at widths above 64, when one chain serves the network.
 const KernelEntry kLayered = {"mlp_layered<256/128/64-wide chains | gemm 256x256 | 128x256, fused epilogue>", 0, {}, true, MLP_LAYOUT_PACKED,
                               MLP_ACT_VECTOR, 256, 64, true, nullptr, nullptr};
 bool is_layered(const KernelEntry *e) { return e == &kLayered; }
@@ -176,6 +176,8 @@ const KernelEntry *select(int n_layers, const int32_t *widths, int layout, int a
             covers &= widths[k] <= all[i].widths[k];
         if (all[i].vec_io && (widths[0] % 8 != 0 || widths[n_layers] % 4 != 0))
             covers = false;  // its vector loads and stores need these widths
+        if (n_layers > MLP_FUSED_MAX_LAYERS && all[i].widths[0] > 64 && mlpk::layered_one_narrow_chain(n_layers, widths))
+            covers = false;  // a deep 128-wide net that one chain serves runs faster layer by layer
         if (covers)
             return &all[i];
     }

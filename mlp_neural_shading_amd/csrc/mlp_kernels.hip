@@ -934,6 +934,16 @@ static const KernelEntry kEntries[] = {
     MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=6>"),
     MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=7>"),
     MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=8>"),
+    // deeper nets with a width above 64 (layers 0-3 in LDS, the rest through the caches), taken only
+    // where the layer-by-layer path would not run the whole network as one chain (which is faster)
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=9>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=10>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=11>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=12>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=13>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=14>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=15>"),
+    MLP_GENERIC128V(128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128, 128)("mlp_fused<generic128v,L=16>"),
     MLP_GENERIC(128, 128)("mlp_fused<generic128,L=1>"),
     MLP_GENERIC(128, 128, 128)("mlp_fused<generic128,L=2>"),
     MLP_GENERIC(128, 128, 128, 128)("mlp_fused<generic128,L=3>"),

@@ -82,6 +82,23 @@ inline int layered_chain_class(int win, int wout)
 // Whether a layer of class k can join a chain that starts with a layer of class k0 (both non-zero).
 inline bool layered_chain_joins(int k0, int k) { return k0 == 256 ? k == 256 : k == 64 || k == 128; }
 
+// Whether the layer-by-layer path runs a whole network (widths w[0..n]) as one chain of 128 or 64
+// padded outputs, given input and output rows that are 16-byte aligned (as mlp_infer requires):
+// every layer in the chain classes, the input width its own padding, the output width a multiple of
+// 8, at most kChainMaxLayers layers.
+inline bool layered_one_narrow_chain(int n, const int32_t *w)
+{
+    if (n < 2 || n > kChainMaxLayers || w[0] != layered_kin(w[0]) || w[n] % 8 != 0)
+        return false;
+    const int k0 = layered_chain_class(w[0], w[1]);
+    if (k0 != 64 && k0 != 128)
+        return false;
+    for (int l = 0; l < n; ++l)
+        if (!layered_chain_joins(k0, layered_chain_class(w[l], w[l + 1])))
+            return false;
+    return true;
+}
+
 hipError_t launch_chain(const ChainArgs &c, hipStream_t stream);
 
 // Rows one workgroup covers (the row tile).

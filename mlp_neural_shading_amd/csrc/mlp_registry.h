@@ -25,7 +25,7 @@ struct LaunchArgs {
 struct KernelEntry {
     const char *name;
     int n_layers;
-    int widths[MLP_FUSED_NARROW_MAX_LAYERS + 1];  // exact instance: the widths it serves; generic: all 64 or all 128 (any shape within)
+    int widths[MLP_FUSED_DEEP_MAX_LAYERS + 1];  // exact instance: the widths it serves; generic: all 64 or all 128 (any shape within)
     bool generic;
     int layout;
     int act;

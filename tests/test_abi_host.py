@@ -153,7 +153,9 @@ def test_plan_widths():
     assert B.mlp_plan_widths([16] * 17) == [64] * 17  # 16 narrow layers: still fused
     assert B.mlp_plan_widths([16] * 18) == [64] + [128] * 17  # 17 layers: layer by layer
     assert B.mlp_plan_widths([12] + [16] * 9) == [64] + [128] * 9  # input width not a multiple of 8
-    assert B.mlp_plan_widths([16] * 9 + [65]) == [64] + [128] * 9  # a width above 64
+    assert B.mlp_plan_widths([16] * 9 + [65]) == [64] + [128] * 9  # 9 layers, output not a multiple of 4
+    assert B.mlp_plan_widths([64] + [128] * 9 + [4]) == [128] * 11  # 10 layers up to 128 wide: fused
+    assert B.mlp_plan_widths([64] * 17) == [64] * 17  # at most 64 wide: fused even where a chain serves
 
 
 # ---- an independent reading of the layer-by-layer image ------------------------------------------

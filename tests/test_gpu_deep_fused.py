@@ -1,8 +1,9 @@
-"""GPU parity of the fused kernel on deep narrow networks: 9 to 16 layers whose widths are all at most
-64 (input width a multiple of 8, output width a multiple of 4) run as one fused dispatch, every layer
-the page's affine layer with the FP16 leaky ReLU between layers ("Profiling neural material
-inference", "Experiment setup" and "Bad versus good activation"), the weights of all layers held in
-LDS.  Against the CPU oracle through the C ABI:
+"""GPU parity of the fused kernel on deep networks: 9 to 16 layers (input width a multiple of 8, output
+width a multiple of 4) run as one fused dispatch when every width is at most 64 (all layers' weights
+in LDS), and at widths up to 128 unless one 128-wide chain of the layer-by-layer path serves the
+whole network; every layer the page's affine layer with the FP16 leaky ReLU between layers
+("Profiling neural material inference", "Experiment setup" and "Bad versus good activation").
+Against the CPU oracle through the C ABI:
 
 - order-free nets (every partial sum exact): bit for bit, against int64 products and the oracle;
 - permutation chains (the leaky slope on negative values through every layer): bit for bit;
@@ -30,18 +31,21 @@ def _x(rows, w, seed):
     return f16(rng.uniform(-1, 1, size=(rows, w))).view(np.uint16)
 
 
-def _widths(rng, L):
-    """L + 1 widths of at most 64: the input a multiple of 8, the output a multiple of 4."""
-    w = [int(v) for v in rng.integers(1, 65, size=L + 1)]
-    w[0] = 8 * int(rng.integers(1, 9))
-    w[-1] = 4 * int(rng.integers(1, 17))
+def _widths(rng, L, hi):
+    """L + 1 widths of at most hi: the input a multiple of 8, the output a multiple of 4."""
+    w = [int(v) for v in rng.integers(1, hi + 1, size=L + 1)]
+    w[0] = 8 * int(rng.integers(1, hi // 8 + 1))
+    w[-1] = 4 * int(rng.integers(1, hi // 4 + 1))
+    if hi > 64:
+        w[L // 2] = int(rng.integers(65, hi + 1))  # one width above 64: the 128-wide family
+        w[-1] = 4 * (2 * int(rng.integers(0, hi // 8)) + 1)  # not a multiple of 8: no whole-network chain
     return w
 
 
-@pytest.mark.parametrize("L", [9, 12, 16])
-def test_integer_exact_deep_nets(oracle_mod, L):
-    rng = np.random.default_rng(900 + L)
-    widths = _widths(rng, L)
+@pytest.mark.parametrize("L,hi", [(9, 64), (12, 64), (16, 64), (10, 128), (16, 128)])
+def test_integer_exact_deep_nets(oracle_mod, L, hi):
+    rng = np.random.default_rng(900 + L + hi)
+    widths = _widths(rng, L, hi)
     W = [np.zeros((widths[l + 1], widths[l]), np.int64) for l in range(L)]
     for l in range(L):
         for r in range(widths[l + 1]):
@@ -56,7 +60,7 @@ def test_integer_exact_deep_nets(oracle_mod, L):
     log("integer-exact deep fused net", widths)
     y = run(Wf, bf, xf.view(np.uint16))
     name = B.mlp_kernel_name(B.MLP_ACT_VECTOR)
-    assert name == "mlp_fused<generic64v,L=%d>" % L, name
+    assert name == "mlp_fused<generic%dv,L=%d>" % (hi, L), name
     assert np.array_equal(y, f16(h).view(np.uint16))
     assert np.array_equal(y, oracle_mod.mlp_forward(Wf, bf, xf, threads=host_threads()))
 
@@ -82,17 +86,20 @@ def test_permutation_chain_16_layers(oracle_mod, rows):
     assert np.array_equal(y, oracle_mod.mlp_forward(Ws, bs, x, threads=host_threads()))
 
 
-@pytest.mark.parametrize("widths,fused", [
-    ((64,) * 10 + (16,), True), ((32,) + (64,) * 15 + (4,), True), ((16,) * 17, True),
-    ((64,) * 17 + (16,), False),         # 17 layers: layer by layer (one 64-wide chain)
-    ((60,) + (64,) * 10 + (16,), False),  # input width not a multiple of 8
+@pytest.mark.parametrize("widths,family", [
+    ((64,) * 10 + (16,), "generic64v"), ((32,) + (64,) * 15 + (4,), "generic64v"), ((16,) * 17, "generic64v"),
+    ((64,) + (128,) * 9 + (4,), "generic128v"), ((96, 100, 128, 64, 120, 40, 64, 128, 72, 8), "generic128v"),
+    ((128,) * 13 + (12,), "generic128v"),     # the output width keeps it off a whole-network chain
+    ((128,) * 14, "layered"),                 # one 128-wide chain serves all 13 layers
+    ((64,) * 17 + (16,), "layered"),          # 17 layers: one 64-wide chain
+    ((60,) + (64,) * 10 + (16,), "layered"),  # input width not a multiple of 8
 ])
-def test_random_weights(oracle_mod, widths, fused):
+def test_random_weights(oracle_mod, widths, family):
     Ws, bs = workloads.init_weights(widths, seed=len(widths))
     x = _x(4096 + 37, widths[0], len(widths) + 3)
     y = run(Ws, bs, x)
     name = B.mlp_kernel_name(B.MLP_ACT_VECTOR)
-    log("deep narrow net", widths[:4], "layers", len(widths) - 1, name)
-    assert name.startswith("mlp_fused<generic64v") == fused, name
+    log("deep net", widths[:4], "layers", len(widths) - 1, name)
+    assert name.startswith("mlp_layered" if family == "layered" else "mlp_fused<%s," % family), name
     stats = compare(y, oracle_mod.mlp_forward(Ws, bs, x, threads=host_threads()), what=str(widths))
     log("  max |d| %.3g, bit-identical %.4f" % (stats["max_abs"], stats["bit_identical_frac"]))
