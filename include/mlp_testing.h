@@ -27,6 +27,12 @@ int mlp_testing_pack_device_on_host(int n_layers, const int32_t *widths, const u
                                     const uint16_t *const *biases, int layout, void *host_dst, size_t dst_bytes,
                                     int *exact_cover);
 
+/* The kernel mlp_pack_weights would select for this shape and layout, by the name mlp_kernel_name
+ * reports once it is packed: a dedicated or generic fused instance, or the layer-by-layer path.
+ *   name  receives the NUL-terminated name (truncated to cap - 1 characters)
+ * Host only; no HIP call.  Errors: INVALID_ARGUMENT, UNSUPPORTED (as mlp_packed_size). */
+int mlp_testing_plan_kernel(int n_layers, const int32_t *widths, int layout, char *name, size_t cap);
+
 #ifdef __cplusplus
 }
 #endif

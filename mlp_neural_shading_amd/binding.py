@@ -39,7 +39,7 @@ EXPORTED = (
     "mlp_infer_ex", "mlp_set_activation_mode", "mlp_kernel_name", "mlp_debug_read_packed",
     "mlp_last_error", "mlp_release",
     # include/mlp_testing.h
-    "mlp_testing_pack_device_on_host",
+    "mlp_testing_pack_device_on_host", "mlp_testing_plan_kernel",
 )
 
 
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
             "mlp_last_error": ([], ctypes.c_char_p),
             "mlp_release": ([], None),
             "mlp_testing_pack_device_on_host": ([i32, p, p, p, i32, p, sz, p], i32),
+            "mlp_testing_plan_kernel": ([i32, p, i32, p, sz], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -211,6 +212,14 @@ def mlp_testing_pack_device_on_host(weights, biases, layout: int = MLP_LAYOUT_PA
     _check(lib().mlp_testing_pack_device_on_host(len(w) - 1, w.ctypes.data, ws.wp, ws.bp, layout, dst.ctypes.data, n,
                                                  ctypes.byref(cover)), "mlp_testing_pack_device_on_host")
     return dst, bool(cover.value)
+
+
+def mlp_testing_plan_kernel(widths, layout: int = MLP_LAYOUT_PACKED) -> str:
+    """The kernel mlp_pack_weights would select for this shape and layout (host only)."""
+    w = _widths(widths)
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().mlp_testing_plan_kernel(len(w) - 1, w.ctypes.data, layout, buf, 256), "mlp_testing_plan_kernel")
+    return buf.value.decode()
 
 
 # ---- torch convenience ------------------------------------------------------------------------

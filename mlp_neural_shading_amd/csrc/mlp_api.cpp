@@ -363,6 +363,18 @@ int mlp_pack_weights(int n_layers, const int32_t *widths, const uint16_t *const 
     return ok();
 }
 
+int mlp_testing_plan_kernel(int n_layers, const int32_t *widths, int layout, char *name, size_t cap)
+{
+    const KernelEntry *e = nullptr;
+    const int rc = plan(n_layers, widths, layout, &e);
+    if (rc != MLP_OK)
+        return rc;
+    if (!name || cap == 0)
+        return fail(MLP_ERR_INVALID_ARGUMENT, "name is NULL or empty");
+    snprintf(name, cap, "%s", e->name);
+    return ok();
+}
+
 int mlp_testing_pack_device_on_host(int n_layers, const int32_t *widths, const uint16_t *const *weights,
                                     const uint16_t *const *biases, int layout, void *host_dst, size_t dst_bytes,
                                     int *exact_cover)

@@ -89,10 +89,39 @@ def test_device_pack_validation():
     assert L.mlp_pack_weights_device(2, w3.ctypes.data, two, two, B.MLP_LAYOUT_ROW_MAJOR, None) == B.MLP_ERR_UNSUPPORTED
 
 
+def test_kernel_selection():
+    """Which kernel each shape takes (mlp.h's fused limits): the dedicated instances for the workload
+    shapes and layouts, the generic 64- and 128-wide families up to 8 layers (element by element
+    without vector I/O), up to 16 layers with vector I/O (at widths above 64 unless one 128-wide chain
+    serves the whole network), else the layer-by-layer path."""
+    plan = B.mlp_testing_plan_kernel
+    assert plan(workloads.get("page").widths) == "mlp_fused<32-64x7-4,packed,vector>"
+    assert plan(workloads.get("page").widths, B.MLP_LAYOUT_ROW_MAJOR) == "mlp_fused<32-64x7-4,rowmajor,vector>"
+    assert plan(workloads.get("wide").widths, B.MLP_LAYOUT_PACKED_FP8) == "mlp_fused_fp8<64-128x7-4>"
+    assert plan([9, 64, 3]) == "mlp_fused<generic64,L=2>"
+    assert plan([8, 64, 4]) == "mlp_fused<generic64v,L=2>"
+    assert plan([9, 65, 3]) == "mlp_fused<generic128,L=2>"
+    assert plan([64] * 9) == "mlp_fused<generic64v,L=8>"
+    assert plan([64] * 17) == "mlp_fused<generic64v,L=16>"  # 16 narrow layers
+    assert plan([64] * 18).startswith("mlp_layered")  # 17 layers
+    assert plan([60] + [64] * 9).startswith("mlp_layered")  # 9 layers without vector I/O
+    assert plan([64] + [128] * 9 + [4]) == "mlp_fused<generic128v,L=10>"
+    assert plan([128] * 13 + [12]) == "mlp_fused<generic128v,L=13>"
+    assert plan([128] * 14).startswith("mlp_layered")  # one 128-wide chain serves all 13 layers
+    assert plan([64] + [128] * 12 + [16]).startswith("mlp_layered")  # likewise, a 64-wide input
+    assert plan([72] + [128] * 12 + [16]) == "mlp_fused<generic128v,L=13>"  # 72 is not its own padding
+    assert plan([64, 256, 16]).startswith("mlp_layered")  # a width above 128
+    with pytest.raises(B.MlpError) as e:
+        plan([64] * 17, B.MLP_LAYOUT_ROW_MAJOR)
+    assert e.value.code == B.MLP_ERR_UNSUPPORTED
+
+
 DEVICE_PACK_CASES = [(name, layout) for name in ["small", "page", "hetero", "wide", "stream"]
                      for layout in (B.MLP_LAYOUT_PACKED, B.MLP_LAYOUT_ROW_MAJOR, B.MLP_LAYOUT_PACKED_FP8)]
 DEVICE_PACK_CASES += [("generic-5-7-3", B.MLP_LAYOUT_PACKED), ("generic-100-30-7", B.MLP_LAYOUT_PACKED),
-                      ("layered-100-300-129-7", B.MLP_LAYOUT_PACKED), ("layered-40x11", B.MLP_LAYOUT_PACKED)]
+                      ("layered-100-300-129-7", B.MLP_LAYOUT_PACKED), ("generic-40x11", B.MLP_LAYOUT_PACKED),
+                      ("generic-32-64x15-12", B.MLP_LAYOUT_PACKED), ("generic-72x10", B.MLP_LAYOUT_PACKED),
+                      ("layered-40x18", B.MLP_LAYOUT_PACKED), ("layered-16x34", B.MLP_LAYOUT_PACKED)]
 
 
 @pytest.mark.parametrize("name,layout", DEVICE_PACK_CASES)
