@@ -17,7 +17,8 @@ inference", section "Experiment setup").  Prints one JSON line:
                the HBM fraction of each
   dispatch     an empty kernel timed the same way, and the wall-clock gap between back-to-back steps
   overlap      mlp_infer on a second stream beside a copy or a GEMM: alone, serial and concurrent times
-  layered      networks beyond the fused kernels (widths > 128, more than 8 layers), layer by layer
+  layered      networks beyond the eight-layer kernels (widths > 128, more than 8 layers): layer by
+               layer, or fused up to 16 layers
   clocks       the GPU clock levels the driver reports before and after the measurements
   cpu_baseline the CPU oracle on a bounded sample of the same rows, one host thread pinned to a core
 """
@@ -261,9 +262,10 @@ def measure_overlap(torch, B, wl, x, y) -> dict:
 
 
 def measure_layered(torch, B, workloads) -> dict:
-    """Networks beyond the fused kernels (one MFMA GEMM per layer with the fused epilogue): median of
-    10 event-timed dispatches after 40 warm-up calls (~40 ms: the first ~10 ms after the GPU has been
-    idle run ~10 % slower while the clock ramps up), FLOPs = 2 * sum w_{l-1} w_l per row."""
+    """Networks beyond the dedicated kernels and the eight-layer limit (layer by layer, or the deep
+    generic fused kernel up to 16 layers): median of 10 event-timed dispatches after 40 warm-up calls
+    (~40 ms: the first ~10 ms after the GPU has been idle run ~10 % slower while the clock ramps up),
+    FLOPs = 2 * sum w_{l-1} w_l per row."""
     res = {}
     dev = torch.device("cuda:0")
     sh = torch.cuda.current_stream().cuda_stream

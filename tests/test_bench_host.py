@@ -57,6 +57,10 @@ def test_layered_workloads_are_named_apart():
     narrow128 = workloads.get("layered128deep")
     assert narrow128.widths == (128,) * 13 + (16,) and narrow128.batch == 1 << 20
     assert B.mlp_plan_widths(narrow128.widths) == [128] * 14
+    fused = workloads.get("deep64fused")  # 16 layers: the deep generic fused kernel, not layer by layer
+    assert fused.widths == (64,) * 16 + (16,) and fused.batch == 1 << 20
+    assert B.mlp_testing_plan_kernel(fused.widths) == "mlp_fused<generic64v,L=16>"
+    assert B.mlp_testing_plan_kernel(narrow.widths).startswith("mlp_layered")
 
 
 def test_layered_workload_refuses_the_row_major_layout():

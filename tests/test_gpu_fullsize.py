@@ -82,7 +82,8 @@ def test_full_size_sampled(oracle_mod, name, n_random, edge):
 # against the oracle (the 1024-wide net costs ~6.4 M multiply-adds per row on the host, the 256-wide
 # one ~1 M, the deep narrow ones 0.07 M and 0.2 M).
 @pytest.mark.parametrize("name,n_random,edge", [("layered1024", 1024, 256), ("layered256", 4096, 1024),
-                                                ("layered64deep", 65536, 4096), ("layered128deep", 16384, 4096)])
+                                                ("layered64deep", 65536, 4096), ("layered128deep", 16384, 4096),
+                                                ("deep64fused", 65536, 4096)])
 def test_layered_workload_full_size_sampled(oracle_mod, name, n_random, edge):
     import torch
 
