@@ -182,9 +182,9 @@ void oracle_leaky_f16_array(int64_t n, const uint16_t *in, uint16_t *out)
 /* the FP8 variant                                                                          */
 /* ---------------------------------------------------------------------------------------- */
 /*
- * A lower-precision form of the same network (the survey's "next" step after the FP16 path; the
- * pages point to lower precisions and to block-scaled formats that carry one power-of-two scale per
- * block of elements).  Readings taken here, listed with the design notes:
+ * A lower-precision form of the same network (beyond the FP16 path, the pages point to lower
+ * precisions and to block-scaled formats that carry one power-of-two scale per block of elements).
+ * Readings taken here, listed with the design notes:
  *   - format: OCP FP8 E4M3 (1 sign bit, 4 exponent bits with bias 7, 3 fraction bits; subnormals
  *     f * 2^-9; the code S.1111.111 is NaN, there is no infinity, the largest finite value is 448);
  *   - conversion to E4M3: round to nearest, ties to even; a magnitude above 464 (the midpoint

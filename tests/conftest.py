@@ -21,7 +21,7 @@ def oracle_mod():
 
 
 def host_threads() -> int:
-    """Worker threads for oracle sharding: the host's cores, capped at 16 (a GPU machine's CPU share)."""
+    """Worker threads for oracle sharding: the host's cores, capped at 16."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
